@@ -1,0 +1,176 @@
+"""ctypes binding of libnvfp4.so (include/nvfp4.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch supplies device memory (``data_ptr``) and the
+current HIP stream.  If the library has not been built, loading raises;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+NVFP4_ERR_INVALID_ARG = -1
+NVFP4_ERR_UNSUPPORTED = -2
+NVFP4_ERR_HIP = -3
+NVFP4_F32 = 0
+NVFP4_BF16 = 1
+NVFP4_GLOBAL_SCALE_GIVEN = 1
+
+EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
+            "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm")
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libnvfp4.so once; raises if it is missing (build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; run `python -m "
+                          "nvfp4_block_scaled_gemm_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.nvfp4_status_string.argtypes = [ctypes.c_int]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_version.argtypes = []
+    lib.nvfp4_version.restype = ctypes.c_char_p
+    lib.nvfp4_quantize_workspace_bytes.argtypes = [i64, i64]
+    lib.nvfp4_quantize_workspace_bytes.restype = sz
+    lib.nvfp4_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, p, ctypes.c_uint,
+                                   p, sz, p]
+    lib.nvfp4_quantize.restype = ctypes.c_int
+    lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, ctypes.c_int, i64, p]
+    lib.nvfp4_gemm.restype = ctypes.c_int
+    lib.nvfp4_grouped_gemm.argtypes = [i32, p, i64, i64, i64, p, p, p, p, p, p, p,
+                                       ctypes.c_int, i64, p]
+    lib.nvfp4_grouped_gemm.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != NVFP4_OK:
+        msg = load().nvfp4_status_string(status).decode()
+        raise Nvfp4Error(fn, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_DT_IN = {torch.float32: NVFP4_F32, torch.bfloat16: NVFP4_BF16}
+_DT_OUT = {"f32": (NVFP4_F32, torch.float32), "bf16": (NVFP4_BF16, torch.bfloat16)}
+
+
+# --------------------------------------------------------------------------
+# raw entry points (same names and arguments as the C ABI)
+# --------------------------------------------------------------------------
+
+def nvfp4_quantize_workspace_bytes(rows: int, cols: int) -> int:
+    return int(load().nvfp4_quantize_workspace_bytes(rows, cols))
+
+
+def nvfp4_quantize_raw(x, x_dtype, rows, cols, ld_x, q, s, global_scale, flags,
+                       workspace, workspace_bytes, stream=None) -> int:
+    return load().nvfp4_quantize(x, x_dtype, rows, cols, ld_x, q, s, global_scale, flags,
+                                 workspace, workspace_bytes, _stream(stream))
+
+
+def nvfp4_gemm_raw(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y, y_dtype, ld_y,
+                   stream=None) -> int:
+    return load().nvfp4_gemm(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y, y_dtype, ld_y,
+                             _stream(stream))
+
+
+def nvfp4_grouped_gemm_raw(G, m_offsets, total_m, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y,
+                           y_dtype, ld_y, stream=None) -> int:
+    return load().nvfp4_grouped_gemm(G, m_offsets, total_m, N, K, a_q, a_s, a_g, b_q, b_s,
+                                     b_g, y, y_dtype, ld_y, _stream(stream))
+
+
+# --------------------------------------------------------------------------
+# tensor-level wrappers (allocate outputs with torch, then call the C ABI)
+# --------------------------------------------------------------------------
+
+def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None,
+                   out=None, workspace: torch.Tensor | None = None, stream=None):
+    """x [rows, cols] fp32/bf16 on the GPU -> (q uint8 [rows, cols/2],
+    s uint8 [rows, cols/16], g fp32 [1]).  ``global_scale`` (device fp32 [1])
+    switches to the static-scale path; ``out`` = (q, s, g) reuses buffers."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1, "x: 2-D, unit column stride, on GPU"
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        q, s, g = out
+    flags = 0
+    if global_scale is not None:
+        g.copy_(global_scale.reshape(1))
+        flags = NVFP4_GLOBAL_SCALE_GIVEN
+    ws_bytes = nvfp4_quantize_workspace_bytes(rows, cols)
+    if workspace is None and flags == 0:
+        workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=dev)
+    st = nvfp4_quantize_raw(_ptr(x), _DT_IN[x.dtype], rows, cols, x.stride(0), _ptr(q), _ptr(s),
+                            _ptr(g), flags, _ptr(workspace),
+                            0 if workspace is None else workspace.numel() * workspace.element_size(),
+                            stream)
+    _check("nvfp4_quantize", st)
+    return q, s, g
+
+
+def nvfp4_gemm(a, b, out_dtype: str = "bf16", y: torch.Tensor | None = None, stream=None):
+    """a = (q, s, g) of x [M, K]; b = (q, s, g) of W [N, K] -> y [M, N]."""
+    a_q, a_s, a_g = a
+    b_q, b_s, b_g = b
+    M, N, K = a_q.shape[0], b_q.shape[0], a_q.shape[1] * 2
+    assert b_q.shape[1] * 2 == K and a_s.shape == (M, K // 16) and b_s.shape == (N, K // 16)
+    code, tdt = _DT_OUT[out_dtype]
+    if y is None:
+        y = torch.empty((M, N), dtype=tdt, device=a_q.device)
+    st = nvfp4_gemm_raw(M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s),
+                        _ptr(b_g), _ptr(y), code, y.stride(0), stream)
+    _check("nvfp4_gemm", st)
+    return y
+
+
+def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: str = "bf16",
+                       y: torch.Tensor | None = None, stream=None):
+    """m_offsets int32 [G+1] (GPU); a = (q [total_m, K/2], s, g [1]);
+    b = (q [G, N, K/2], s [G, N, K/16], g [G]) -> y [total_m, N]."""
+    a_q, a_s, a_g = a
+    b_q, b_s, b_g = b
+    G, N = b_q.shape[0], b_q.shape[1]
+    K = b_q.shape[2] * 2
+    assert m_offsets.dtype == torch.int32 and m_offsets.numel() == G + 1
+    code, tdt = _DT_OUT[out_dtype]
+    if y is None:
+        y = torch.empty((total_m, N), dtype=tdt, device=b_q.device)
+    st = nvfp4_grouped_gemm_raw(G, _ptr(m_offsets), total_m, N, K, _ptr(a_q), _ptr(a_s),
+                                _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
+                                y.stride(0), stream)
+    _check("nvfp4_grouped_gemm", st)
+    return y

@@ -1,0 +1,112 @@
+// C ABI of the NVFP4 library (include/nvfp4.h): host-side argument checks and
+// shape dispatch.  All checks run before anything is enqueued, so invalid
+// calls return an error without touching the GPU.
+#include "nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "nvfp4_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps 32-bit tile indexing safe
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// Common checks of one packed operand [rows, K].
+bool operand_ok(int64_t rows, int64_t K, const uint8_t* q, const uint8_t* s, const float* g) {
+  if (rows == 0 || K == 0) return g != nullptr;
+  return q != nullptr && s != nullptr && g != nullptr;
+}
+
+// Kernel eligibility for the tiled paths: 16-byte aligned nibble rows and
+// 8-byte aligned scale rows.
+bool tiled_ok(int64_t K, const uint8_t* q, const uint8_t* s, int64_t kmult) {
+  return K % kmult == 0 && aligned(q, 16) && aligned(s, 8);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_INVALID_ARG: return "NVFP4_ERR_INVALID_ARG";
+    case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP";
+    default: return "NVFP4_UNKNOWN_STATUS";
+  }
+}
+
+const char* nvfp4_version(void) { return "0.1.0"; }
+
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return nvfp4::quantize_workspace_bytes(rows, cols);
+}
+
+int nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                   int64_t ld_x, uint8_t* q, uint8_t* s, float* global_scale, unsigned flags,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (flags & ~NVFP4_GLOBAL_SCALE_GIVEN) return NVFP4_ERR_INVALID_ARG;
+  if (global_scale == nullptr) return NVFP4_ERR_INVALID_ARG;
+  if (rows > kMaxDim || cols > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (x == nullptr || q == nullptr || s == nullptr) return NVFP4_ERR_INVALID_ARG;
+  if (ld_x < cols) return NVFP4_ERR_INVALID_ARG;
+  const bool given = (flags & NVFP4_GLOBAL_SCALE_GIVEN) != 0;
+  if (!given) {
+    if (workspace == nullptr || !aligned(workspace, 4)) return NVFP4_ERR_INVALID_ARG;
+    if (workspace_bytes < nvfp4::quantize_workspace_bytes(rows, cols))
+      return NVFP4_ERR_INVALID_ARG;
+  }
+  const int64_t esz = x_dtype == NVFP4_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ld_x * esz) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(q, 8)) return NVFP4_ERR_UNSUPPORTED;
+  return from_hip(nvfp4::launch_quantize(x, (int)x_dtype, rows, cols, ld_x, q, s, global_scale,
+                                         given, workspace, (hipStream_t)stream));
+}
+
+int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+               const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+               void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (y == nullptr || ld_y < N) return NVFP4_ERR_INVALID_ARG;
+  if (!operand_ok(M, K, a_q, a_s, a_g) || !operand_ok(N, K, b_q, b_s, b_g))
+    return NVFP4_ERR_INVALID_ARG;
+  const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = (int)y_dtype;
+  // K == 0: the sum is empty; the general kernel writes zeros.
+  if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128))
+    return from_hip(nvfp4::launch_gemm_mfma(M, N, K, a, b, y, dt, ld_y, st));
+  return from_hip(nvfp4::launch_gemm_generic(M, N, K, a, b, y, dt, ld_y, st));
+}
+
+int nvfp4_grouped_gemm(int32_t G, const int32_t* m_offsets, int64_t total_m, int64_t N,
+                       int64_t K, const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                       const uint8_t* b_q, const uint8_t* b_s, const float* b_g, void* y,
+                       nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {
+  if (G < 0 || total_m < 0 || N < 0 || K < 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (G == 0 && total_m != 0) return NVFP4_ERR_INVALID_ARG;
+  if (total_m > kMaxDim || N > kMaxDim || K > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
+  if (total_m == 0 || N == 0) return NVFP4_OK;
+  if (m_offsets == nullptr || y == nullptr || ld_y < N) return NVFP4_ERR_INVALID_ARG;
+  if (!operand_ok(total_m, K, a_q, a_s, a_g) || !operand_ok(N, K, b_q, b_s, b_g))
+    return NVFP4_ERR_INVALID_ARG;
+  const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
+  hipStream_t st = (hipStream_t)stream;
+  return from_hip(nvfp4::launch_gemm_grouped_generic(G, m_offsets, total_m, N, K, a, b, y,
+                                                     (int)y_dtype, ld_y, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// General NVFP4 GEMM for shapes the tiled kernels do not take (K not a
+// multiple of the tile depth, unaligned rows).  One thread per output element;
+// each 16-element block product is formed exactly in integers and scaled
+// exactly in fp32, and the block contributions are summed in fp32 in K order.
+//
+// y[m, n] = fl32(ga * gb) * sum_k A(m, k) B(n, k)   (kernelindex "NVFP4 linear
+// layer", description: y = x @ W^T with E2M1 operands and E4M3FN scales per
+// 16 elements).  With m_offsets given, row m uses weight group e where
+// m_offsets[e] <= m < m_offsets[e+1] (grouped form).
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+namespace {
+
+// 2 * E2M1 magnitude of code c = 0..7 is 0,1,2,3,4,6,8,12: one hex digit each
+// of 0xC8643210, read at digit c; bit 3 of the nibble is the sign.
+__device__ __forceinline__ int e2m1_x2(uint32_t nib) {
+  const int mag = (int)((0xC8643210u >> (4u * (nib & 7u))) & 15u);
+  return (nib & 8u) ? -mag : mag;
+}
+
+__global__ __launch_bounds__(256) void gemm_generic_kernel(
+    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_q,
+    const uint8_t* __restrict__ a_s, const float* __restrict__ a_g,
+    const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
+    const float* __restrict__ b_g, const int32_t* __restrict__ m_offsets, int32_t G,
+    void* __restrict__ y, int y_dtype, int64_t ld_y) {
+  const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
+  const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
+  if (m >= M || n >= N) return;
+  int64_t e = 0;
+  if (m_offsets != nullptr) {
+    // last group e with m_offsets[e] <= m (non-decreasing offsets)
+    int32_t lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if ((int64_t)m_offsets[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+  }
+  const int64_t nblk = K / 16;
+  const uint8_t* aq = a_q + m * (K / 2);
+  const uint8_t* as = a_s + m * nblk;
+  const uint8_t* bq = b_q + (e * N + n) * (K / 2);
+  const uint8_t* bs = b_s + (e * N + n) * nblk;
+  float acc = 0.0f;
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    int isum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t xa = aq[blk * 8 + j], xb = bq[blk * 8 + j];
+      isum += e2m1_x2(xa & 15u) * e2m1_x2(xb & 15u);
+      isum += e2m1_x2(xa >> 4) * e2m1_x2(xb >> 4);
+    }
+    const float sc = e4m3_to_f32(as[blk]) * e4m3_to_f32(bs[blk]);  // exact
+    acc += sc * ((float)isum * 0.25f);                                 // exact term
+  }
+  const float alpha = a_g[0] * b_g[e];
+  store_out(y, m * ld_y + n, acc * alpha, y_dtype);
+}
+
+hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
+                  const int32_t* m_offsets, int32_t G, void* y, int y_dtype, int64_t ld_y,
+                  hipStream_t stream) {
+  // grid.y is limited to 65535 row tiles; larger M is split into chunks
+  const int64_t max_rows = 65535LL * 16;
+  for (int64_t m0 = 0; m0 < M; m0 += max_rows) {
+    const int64_t rows = (M - m0 < max_rows) ? (M - m0) : max_rows;
+    dim3 grid((unsigned)((N + 15) / 16), (unsigned)((rows + 15) / 16));
+    // chunks past the first shift A and y; the group search sees global rows
+    // only through m_offsets, so chunking is used for the dense case alone
+    gemm_generic_kernel<<<grid, 256, 0, stream>>>(
+        rows, N, K, a.q + m0 * (K / 2), a.s + m0 * (K / 16), a.g, b.q, b.s, b.g, m_offsets, G,
+        y_dtype == 0 ? (void*)((float*)y + m0 * ld_y) : (void*)((uint16_t*)y + m0 * ld_y),
+        y_dtype, ld_y);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_generic(int64_t M, int64_t N, int64_t K, PackedOperand a,
+                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,
+                               hipStream_t stream) {
+  return launch(M, N, K, a, b, nullptr, 1, y, y_dtype, ld_y, stream);
+}
+
+hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets, int64_t total_m,
+                                       int64_t N, int64_t K, PackedOperand a, PackedOperand b,
+                                       void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
+  if (total_m > 65535LL * 16) return hipErrorInvalidValue;
+  return launch(total_m, N, K, a, b, m_offsets, G, y, y_dtype, ld_y, stream);
+}
+
+}  // namespace nvfp4

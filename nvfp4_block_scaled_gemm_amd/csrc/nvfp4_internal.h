@@ -1,0 +1,48 @@
+// Host-side launchers shared between the C ABI (api.cpp) and the kernel files.
+// Every launcher assumes its arguments were validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace nvfp4 {
+
+// quantize.hip
+size_t quantize_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           uint8_t* q, uint8_t* s, float* gscale, bool scale_given,
+                           void* workspace, hipStream_t stream);
+
+// Operand description of one packed NVFP4 matrix [rows, K].
+struct PackedOperand {
+  const uint8_t* q;  // [rows, K/2]
+  const uint8_t* s;  // [rows, K/16]
+  const float* g;    // device scalar (or [G] for grouped weights)
+};
+
+// gemm_generic.hip: any M, N, K % 16 == 0.
+hipError_t launch_gemm_generic(int64_t M, int64_t N, int64_t K, PackedOperand a,
+                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,
+                               hipStream_t stream);
+
+hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets, int64_t total_m,
+                                       int64_t N, int64_t K, PackedOperand a, PackedOperand b,
+                                       void* y, int y_dtype, int64_t ld_y, hipStream_t stream);
+
+// gemm_mfma.hip: K % 128 == 0, 16-byte aligned operand rows.
+hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a,
+                            PackedOperand b, void* y, int y_dtype, int64_t ld_y,
+                            hipStream_t stream);
+
+// gemm_decode.hip: M <= 32, K % 256 == 0.
+hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a,
+                              PackedOperand b, void* y, int y_dtype, int64_t ld_y,
+                              hipStream_t stream);
+
+// gemm_grouped.hip: K % 256 == 0.
+hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, int64_t total_m,
+                               int64_t N, int64_t K, PackedOperand a, PackedOperand b,
+                               void* y, int y_dtype, int64_t ld_y, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/nvfp4.h declares, and rejects invalid arguments on the host before
+anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_gemm_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+# Fake, never-dereferenced device addresses (validation fails before use).
+P16 = ctypes.c_void_p(0x10000)
+P8 = ctypes.c_void_p(0x10008)
+P4 = ctypes.c_void_p(0x10004)
+NULL = None
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = nv.load()
+    declared = _declared_functions()
+    assert set(declared) == set(nv.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = nv.load()
+    assert lib.nvfp4_status_string(0) == b"NVFP4_OK"
+    assert lib.nvfp4_status_string(-1) == b"NVFP4_ERR_INVALID_ARG"
+    assert lib.nvfp4_status_string(-2) == b"NVFP4_ERR_UNSUPPORTED"
+    assert lib.nvfp4_status_string(-3) == b"NVFP4_ERR_HIP"
+    assert lib.nvfp4_status_string(7) == b"NVFP4_UNKNOWN_STATUS"
+    assert re.fullmatch(rb"\d+\.\d+\.\d+", lib.nvfp4_version())
+
+
+def test_workspace_bytes():
+    assert nv.nvfp4_quantize_workspace_bytes(0, 16) == 0
+    assert nv.nvfp4_quantize_workspace_bytes(16, 0) == 0
+    assert nv.nvfp4_quantize_workspace_bytes(1, 16) == 4
+    w = nv.nvfp4_quantize_workspace_bytes(4096, 8192)
+    assert 4 <= w <= 4096 and w % 4 == 0
+
+
+def _q(**kw):
+    args = dict(x=P16, x_dtype=nv.NVFP4_BF16, rows=4, cols=32, ld_x=32, q=P16, s=P16,
+                global_scale=P16, flags=0, workspace=P16, workspace_bytes=1024)
+    args.update(kw)
+    lib = nv.load()
+    return lib.nvfp4_quantize(args["x"], args["x_dtype"], args["rows"], args["cols"],
+                              args["ld_x"], args["q"], args["s"], args["global_scale"],
+                              args["flags"], args["workspace"], args["workspace_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cols=24), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(rows=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x_dtype=5), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(flags=2), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(global_scale=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(q=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(s=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(ld_x=16), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(workspace=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(workspace_bytes=0), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(workspace=ctypes.c_void_p(0x10002)), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=P8), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(ld_x=36), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(q=P4), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(rows=1 << 31), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(rows=0), nv.NVFP4_OK),
+    (dict(cols=0, ld_x=0), nv.NVFP4_OK),
+])
+def test_quantize_argument_checks(kw, status):
+    assert _q(**kw) == status
+
+
+def _g(**kw):
+    args = dict(M=8, N=8, K=128, a_q=P16, a_s=P16, a_g=P16, b_q=P16, b_s=P16, b_g=P16,
+                y=P16, y_dtype=nv.NVFP4_BF16, ld_y=8)
+    args.update(kw)
+    return nv.load().nvfp4_gemm(*[args[k] for k in ("M", "N", "K", "a_q", "a_s", "a_g", "b_q",
+                                                    "b_s", "b_g", "y", "y_dtype", "ld_y")],
+                                None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=24), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(M=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(N=-3), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y_dtype=2), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(ld_y=7), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(a_q=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(b_s=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(a_g=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(b_g=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(K=1 << 31), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(M=0), nv.NVFP4_OK),
+    (dict(N=0, ld_y=0), nv.NVFP4_OK),
+])
+def test_gemm_argument_checks(kw, status):
+    assert _g(**kw) == status
+
+
+def _gg(**kw):
+    args = dict(G=4, m_offsets=P16, total_m=8, N=8, K=128, a_q=P16, a_s=P16, a_g=P16,
+                b_q=P16, b_s=P16, b_g=P16, y=P16, y_dtype=nv.NVFP4_BF16, ld_y=8)
+    args.update(kw)
+    order = ("G", "m_offsets", "total_m", "N", "K", "a_q", "a_s", "a_g", "b_q", "b_s", "b_g",
+             "y", "y_dtype", "ld_y")
+    return nv.load().nvfp4_grouped_gemm(*[args[k] for k in order], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=40), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(G=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(G=0), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(m_offsets=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(ld_y=4), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(b_q=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y_dtype=9), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(total_m=0), nv.NVFP4_OK),
+    (dict(G=0, total_m=0), nv.NVFP4_OK),
+    (dict(N=0, ld_y=0), nv.NVFP4_OK),
+])
+def test_grouped_argument_checks(kw, status):
+    assert _gg(**kw) == status
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import nvfp4_block_scaled_gemm_amd._lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        L.load()

@@ -1,0 +1,191 @@
+"""GPU GEMM vs the oracle, through the C ABI.
+
+Operands are quantised by the oracle on the CPU and uploaded, so the GEMM is
+checked independently of the GPU quantiser (whose bytes are compared to the
+same oracle output where the GPU quantiser is used).  Tolerance: |y - y_ref|
+<= 1e-5 * sum_k |x_k w_k| per element, plus one bf16 ulp for bf16 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_gemm_amd as nv
+import workloads as wl
+from oracle import check_gemm, e4m3_decode, gemm_ref, pack_nibbles
+from tests.gpu_util import (assert_bytes_equal, need_gpu, note, np_, oracle_global_scale,
+                            oracle_quantize, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemm(a, b, out):
+    y = nv.nvfp4_gemm(a, b, out_dtype=out)
+    torch.cuda.synchronize()
+    return y
+
+
+def _parity(x_cpu, w_cpu, out="f32", tag=""):
+    need_gpu()
+    ra = oracle_quantize(x_cpu)
+    rb = oracle_quantize(w_cpu)
+    note(f"gemm {tag} M={x_cpu.shape[0]} N={w_cpu.shape[0]} K={x_cpu.shape[1]} out={out}")
+    y = _gemm(to_gpu(*ra), to_gpu(*rb), out)
+    y_ref, bound = gemm_ref(*ra, *rb)
+    ok, worst = check_gemm(np_(y), y_ref, bound, out)
+    assert ok, f"{tag}: worst |err|/tol = {worst}"
+    return y, ra, rb
+
+
+def _rand_packed(rng, rows, K, lo=0x20, hi=0x50):
+    q = rng.integers(0, 256, size=(rows, K // 2)).astype(np.uint8)
+    s = rng.integers(lo, hi + 1, size=(rows, K // 16)).astype(np.uint8)
+    return q, s
+
+
+def test_tiny_workload():
+    x, w = wl.gemm_inputs(0, wl.TINY)
+    y, ra, rb = _parity(x, w, "f32", "tiny")
+    # the GPU quantiser produces the same operands
+    for t, ref in ((x, ra), (w, rb)):
+        assert_bytes_equal(*nv.nvfp4_quantize(t.cuda()), *ref)
+
+
+@pytest.mark.parametrize("M", [128, 16, 1])
+def test_exhaustive_dequant_identity(M):
+    """A = first M rows of I_128 (nibble 1.0, scale 1.0, g = 1); W [32, 128]
+    holds every nibble under every finite scale byte, so y = W_dq^T exactly."""
+    need_gpu()
+    K, N = 128, 32
+    nib = np.zeros((M, K), dtype=np.uint8)
+    for i in range(M):
+        nib[i, i] = 0x2
+    a = (pack_nibbles(nib), np.full((M, K // 16), 0x38, np.uint8), np.float32(1))
+    codes = np.arange(256, dtype=np.uint8)
+    codes[0x7F], codes[0xFF] = 0x3F, 0xBF                 # NaN codes replaced
+    rng = np.random.default_rng(0)
+    wn = np.zeros((N, K), dtype=np.uint8)
+    for blk in range(N * K // 16):
+        r, c = divmod(blk, K // 16)
+        wn[r, 16 * c:16 * c + 16] = rng.permutation(16)
+    b = (pack_nibbles(wn), codes.reshape(N, K // 16), np.float32(1))
+    note(f"exhaustive dequant M={M}")
+    y = np_(_gemm(to_gpu(*a), to_gpu(*b), "f32"))
+    y_ref, _ = gemm_ref(*a, *b)
+    assert np.array_equal(y, y_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("M", list(range(1, 65)))
+def test_every_small_m(M):
+    need_gpu()
+    rng = np.random.default_rng(M)
+    K, N = 512, 200
+    a = (*_rand_packed(rng, M, K), np.float32(0.03))
+    b = (*_rand_packed(rng, N, K), np.float32(0.5))
+    y = np_(_gemm(to_gpu(*a), to_gpu(*b), "f32"))
+    y_ref, bound = gemm_ref(*a, *b)
+    ok, worst = check_gemm(y, y_ref, bound, "f32")
+    assert ok, worst
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 128), (7, 129, 384), (300, 260, 256), (257, 255, 1024), (33, 96, 48),
+    (5, 7, 16), (129, 3, 2048), (600, 520, 640), (64, 64, 8192),
+])
+def test_odd_shapes(M, N, K):
+    need_gpu()
+    rng = np.random.default_rng(M * 7 + N + K)
+    a = (*_rand_packed(rng, M, K, 0x00, 0x7E), np.float32(0.7))
+    b = (*_rand_packed(rng, N, K, 0x00, 0x7E), np.float32(1.3))
+    for out in ("f32", "bf16"):
+        note(f"odd shape M={M} N={N} K={K} out={out}")
+        y = np_(_gemm(to_gpu(*a), to_gpu(*b), out))
+        y_ref, bound = gemm_ref(*a, *b)
+        ok, worst = check_gemm(y, y_ref, bound, out)
+        assert ok, (out, worst)
+
+
+def test_k_zero_gives_zeros():
+    need_gpu()
+    dev = "cuda"
+    e = torch.empty((4, 0), dtype=torch.uint8, device=dev)
+    g = torch.ones(1, device=dev)
+    y = torch.full((4, 6), 7.0, device=dev)
+    st = nv.nvfp4_gemm_raw(4, 6, 0, e.data_ptr(), e.data_ptr(), g.data_ptr(), e.data_ptr(),
+                           e.data_ptr(), g.data_ptr(), y.data_ptr(), nv.NVFP4_F32, 6)
+    assert st == nv.NVFP4_OK
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0
+
+
+def test_bf16_output_is_rne_of_f32_and_repeatable():
+    need_gpu()
+    rng = np.random.default_rng(1)
+    for M in (4, 32, 300):
+        a = to_gpu(*_rand_packed(rng, M, 1024), np.float32(0.01))
+        b = to_gpu(*_rand_packed(rng, 384, 1024), np.float32(0.2))
+        y32 = _gemm(a, b, "f32")
+        y16 = _gemm(a, b, "bf16")
+        assert torch.equal(y32.to(torch.bfloat16), y16)
+        assert torch.equal(_gemm(a, b, "f32"), y32)
+
+
+def test_linear_workload_sampled():
+    """M=4096, N=K=8192 bf16 inputs quantised on the GPU (bytes checked on the
+    sampled rows), GEMM in bf16 checked on a 256 x 256 sample of outputs."""
+    need_gpu()
+    x_cpu, w_cpu = wl.gemm_inputs(1, wl.LINEAR)
+    note("linear workload quantize")
+    a = nv.nvfp4_quantize(x_cpu.cuda())
+    b = nv.nvfp4_quantize(w_cpu.cuda())
+    note("linear workload gemm")
+    y = _gemm(a, b, "bf16")
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(wl.LINEAR.M, 256, replace=False))
+    cols = np.sort(rng.choice(wl.LINEAR.N, 256, replace=False))
+    ra = oracle_quantize(x_cpu[torch.from_numpy(rows)], oracle_global_scale(x_cpu))
+    rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
+    assert_bytes_equal(*a, *ra, rows=rows)
+    assert_bytes_equal(*b, *rb, rows=cols)
+    y_ref, bound = gemm_ref(*ra, *rb)
+    ok, worst = check_gemm(np_(y)[np.ix_(rows, cols)], y_ref, bound, "bf16")
+    assert ok, worst
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_decode_workload(M):
+    need_gpu()
+    cfg = wl.DECODE[M]
+    x_cpu, w_cpu = wl.gemm_inputs(2, cfg)
+    a = nv.nvfp4_quantize(x_cpu.cuda())
+    b = nv.nvfp4_quantize(w_cpu.cuda())
+    note(f"decode M={M}")
+    y = _gemm(a, b, "bf16")
+    cols = np.sort(np.random.default_rng(M).choice(cfg.N, 1024, replace=False))
+    ra = oracle_quantize(x_cpu)
+    rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
+    assert_bytes_equal(*a, *ra)
+    assert_bytes_equal(*b, *rb, rows=cols)
+    y_ref, bound = gemm_ref(*ra, *rb)
+    ok, worst = check_gemm(np_(y)[:, cols], y_ref, bound, "bf16")
+    assert ok, worst
+
+
+def test_large_outlier_workload_sampled():
+    need_gpu()
+    c = wl.LARGE
+    x_cpu, w_cpu = wl.gemm_inputs(4, c)
+    note("large workload quantize")
+    a = nv.nvfp4_quantize(x_cpu.cuda())
+    b = nv.nvfp4_quantize(w_cpu.cuda())
+    note("large workload gemm")
+    y = _gemm(a, b, "bf16")
+    rng = np.random.default_rng(4)
+    rows = np.sort(rng.choice(c.M, 64, replace=False))
+    cols = np.sort(rng.choice(c.N, 128, replace=False))
+    ra = oracle_quantize(x_cpu[torch.from_numpy(rows)], oracle_global_scale(x_cpu))
+    rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
+    assert_bytes_equal(*a, *ra, rows=rows)
+    assert_bytes_equal(*b, *rb, rows=cols)
+    y_ref, bound = gemm_ref(*ra, *rb)
+    ok, worst = check_gemm(np_(y)[np.ix_(rows, cols)], y_ref, bound, "bf16")
+    assert ok, worst

@@ -1,0 +1,109 @@
+"""GPU grouped (per-expert) GEMM vs the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_gemm_amd as nv
+import workloads as wl
+from oracle import check_gemm, gemm_ref, grouped_gemm_ref
+from tests.gpu_util import (assert_bytes_equal, need_gpu, note, np_, oracle_global_scale,
+                            oracle_quantize)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_packed(rng, shape_rows, K):
+    q = rng.integers(0, 256, size=(*shape_rows, K // 2)).astype(np.uint8)
+    s = rng.integers(0x10, 0x60, size=(*shape_rows, K // 16)).astype(np.uint8)
+    return q, s
+
+
+def _run(counts, N, K, out, seed):
+    need_gpu()
+    rng = np.random.default_rng(seed)
+    G = len(counts)
+    off = wl.ragged_offsets(counts)
+    total = int(off[-1])
+    aq, as_ = _rand_packed(rng, (total,), K)
+    ag = np.float32(0.05)
+    bq, bs = _rand_packed(rng, (G, N), K)
+    bg = (rng.random(G) + 0.5).astype(np.float32)
+    dev = "cuda"
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)  # noqa: E731
+    note(f"grouped G={G} total={total} N={N} K={K} out={out}")
+    y = nv.nvfp4_grouped_gemm(off.to(dev), total, (t(aq), t(as_), torch.tensor([ag], device=dev)),
+                              (t(bq), t(bs), t(bg)), out_dtype=out)
+    torch.cuda.synchronize()
+    y_ref, bound = grouped_gemm_ref(off.numpy(), aq, as_, ag, bq, bs, bg)
+    ok, worst = check_gemm(np_(y), y_ref, bound, out)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([3, 0, 5, 1, 0, 40], 96, 256),
+    ([0, 0, 7], 64, 512),
+    ([17], 48, 2048),
+    ([1] * 20, 40, 256),
+    ([33, 64, 2, 0, 31, 32, 130], 200, 768),
+    ([5, 9], 30, 48),
+])
+def test_ragged_groups(counts, N, K):
+    for out in ("f32", "bf16"):
+        _run(counts, N, K, out, seed=sum(counts) + N + K)
+
+
+def test_all_groups_empty_but_last():
+    _run([0] * 15 + [4], 64, 256, "f32", seed=3)
+
+
+def _moe_case(proj: str):
+    """MoE workload, one projection: 512 tokens routed top-8 over 256 experts."""
+    need_gpu()
+    N, K = wl.MOE_GATE_UP if proj == "gate_up" else wl.MOE_DOWN
+    routing = wl.moe_routing(wl.seed_for(3, 0))
+    E = wl.MOE_EXPERTS
+    total = int(routing.m_offsets[-1])
+    dev = "cuda"
+    if proj == "gate_up":
+        x_cpu = wl.randn((wl.MOE_TOKENS, K), wl.seed_for(3, 1), "bf16")
+        q, s, g = nv.nvfp4_quantize(x_cpu.cuda())
+        rt = routing.row_token.to(dev)
+        a = (q.index_select(0, rt), s.index_select(0, rt), g)
+        rows_tok = routing.row_token
+    else:
+        x_cpu = wl.randn((total, K), wl.seed_for(3, 2), "bf16")
+        a = nv.nvfp4_quantize(x_cpu.cuda())
+        rows_tok = torch.arange(total)
+    bq = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    bs = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
+    bg = torch.empty((E,), dtype=torch.float32, device=dev)
+    wseed = lambda e: wl.seed_for(3, (100 if proj == "gate_up" else 1000) + e)  # noqa: E731
+    note(f"moe {proj}: quantizing {E} experts")
+    for e in range(E):
+        w = wl.randn((N, K), wseed(e), "bf16", device=dev)
+        nv.nvfp4_quantize(w, out=(bq[e], bs[e], bg[e:e + 1]))
+    note(f"moe {proj}: grouped gemm")
+    y = nv.nvfp4_grouped_gemm(routing.m_offsets.to(dev), total, a, (bq, bs, bg), "bf16")
+    torch.cuda.synchronize()
+    y_np = np_(y)
+    ga = oracle_global_scale(x_cpu)
+    cols = np.sort(np.random.default_rng(7).choice(N, 256, replace=False))
+    off = routing.m_offsets.numpy()
+    for e in (0, 97, 255):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        assert r1 > r0
+        w_cpu = wl.randn((N, K), wseed(e), "bf16", device=dev).cpu()
+        rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
+        assert_bytes_equal(bq[e], bs[e], bg[e:e + 1], *rb, rows=cols)
+        ra = oracle_quantize(x_cpu[rows_tok[r0:r1]], ga)
+        y_ref, bound = gemm_ref(*ra, *rb)
+        ok, worst = check_gemm(y_np[r0:r1][:, cols], y_ref, bound, "bf16")
+        assert ok, (e, worst)
+
+
+def test_moe_gate_up():
+    _moe_case("gate_up")
+
+
+def test_moe_down():
+    _moe_case("down")
