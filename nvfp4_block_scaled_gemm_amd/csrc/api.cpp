@@ -86,6 +86,8 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_
   hipStream_t st = (hipStream_t)stream;
   const int dt = (int)y_dtype;
   // K == 0: the sum is empty; the general kernel writes zeros.
+  if (K > 0 && M <= 32 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256))
+    return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st));
   if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128))
     return from_hip(nvfp4::launch_gemm_mfma(M, N, K, a, b, y, dt, ld_y, st));
   return from_hip(nvfp4::launch_gemm_generic(M, N, K, a, b, y, dt, ld_y, st));
@@ -105,6 +107,9 @@ int nvfp4_grouped_gemm(int32_t G, const int32_t* m_offsets, int64_t total_m, int
     return NVFP4_ERR_INVALID_ARG;
   const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
   hipStream_t st = (hipStream_t)stream;
+  if (K > 0 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256))
+    return from_hip(nvfp4::launch_gemm_grouped(G, m_offsets, total_m, N, K, a, b, y,
+                                               (int)y_dtype, ld_y, st));
   return from_hip(nvfp4::launch_gemm_grouped_generic(G, m_offsets, total_m, N, K, a, b, y,
                                                      (int)y_dtype, ld_y, st));
 }

@@ -30,28 +30,29 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
 }
 
-// Four packed FP4 bytes (8 nibbles, element 2j in the low nibble of byte j)
-// -> 8 fp16 values E2M1 * scale.  The hardware converts each byte into two
-// fp16 (low nibble first) with a unit scale; the per-block E4M3 factor is then
-// applied with one packed fp16 multiply per pair, exact by the argument above.
-__device__ __forceinline__ f16x8 dequant8(uint32_t packed, f16x2 scale2) {
-  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 0);
-  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 1);
-  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2);
-  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 3);
-  p0 *= scale2;
-  p1 *= scale2;
-  p2 *= scale2;
-  p3 *= scale2;
+// {S, S} as fp16 bits with S = E4M3(byte) * 2^-8: E4M3 and fp16 share the
+// subnormal/normal structure, so the 7 magnitude bits shifted left by 7 are
+// exactly E4M3 * 2^-8 in fp16 (possibly subnormal); the sign moves to bit 15.
+// The factor 2^8 is restored by converting nibbles with a scale of 256.
+__device__ __forceinline__ uint32_t scale_pair_bits(uint32_t byte) {
+  const uint32_t h = ((byte & 0x7Fu) << 7) | ((byte & 0x80u) << 8);
+  return h | (h << 16);
+}
+
+__device__ __forceinline__ f16x8 dequant8_scaled(uint32_t packed, uint32_t pair_bits) {
+  f16x2 s2;
+  __builtin_memcpy(&s2, &pair_bits, 4);
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 0);
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 1);
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 2);
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 3);
+  p0 *= s2;
+  p1 *= s2;
+  p2 *= s2;
+  p3 *= s2;
   f16x8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-__device__ __forceinline__ f16x2 scale_f16x2(uint32_t byte) {
-  _Float16 h = (_Float16)e4m3_to_f32(byte);
-  f16x2 r = {h, h};
   return r;
 }
 

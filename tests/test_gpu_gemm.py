@@ -50,12 +50,14 @@ def test_tiny_workload():
         assert_bytes_equal(*nv.nvfp4_quantize(t.cuda()), *ref)
 
 
-@pytest.mark.parametrize("M", [128, 16, 1])
-def test_exhaustive_dequant_identity(M):
-    """A = first M rows of I_128 (nibble 1.0, scale 1.0, g = 1); W [32, 128]
-    holds every nibble under every finite scale byte, so y = W_dq^T exactly."""
+@pytest.mark.parametrize("M,K", [(128, 128), (16, 128), (1, 128), (256, 256), (32, 256),
+                                 (1, 256), (20, 256)])
+def test_exhaustive_dequant_identity(M, K):
+    """A = first M rows of I_K (nibble 1.0, scale 1.0, g = 1); W [4096/K, K]
+    holds every nibble under every finite scale byte, so y = W_dq^T exactly
+    (K = 128 runs the tile kernel, K = 256 with M <= 32 the skinny kernel)."""
     need_gpu()
-    K, N = 128, 32
+    N = 4096 // K
     nib = np.zeros((M, K), dtype=np.uint8)
     for i in range(M):
         nib[i, i] = 0x2
@@ -90,6 +92,7 @@ def test_every_small_m(M):
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 128), (7, 129, 384), (300, 260, 256), (257, 255, 1024), (33, 96, 48),
     (5, 7, 16), (129, 3, 2048), (600, 520, 640), (64, 64, 8192),
+    (3, 1000, 2560), (32, 33, 256), (17, 4100, 1024), (31, 70, 16384), (2, 31, 768),
 ])
 def test_odd_shapes(M, N, K):
     need_gpu()
