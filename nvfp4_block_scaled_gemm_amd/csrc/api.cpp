@@ -27,6 +27,9 @@ bool tiled_ok(int64_t K, const uint8_t* q, const uint8_t* s, int64_t kmult) {
   return K % kmult == 0 && aligned(q, 16) && aligned(s, 8);
 }
 
+// The MFMA tile kernel addresses each operand with 32-bit byte offsets.
+bool offsets32_ok(int64_t rows, int64_t K) { return rows * (K / 2) < ((int64_t)1 << 32); }
+
 }  // namespace
 
 extern "C" {
@@ -88,7 +91,8 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_
   // K == 0: the sum is empty; the general kernel writes zeros.
   if (K > 0 && M <= 32 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256))
     return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st));
-  if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128))
+  if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128) &&
+      offsets32_ok(M, K) && offsets32_ok(N, K))
     return from_hip(nvfp4::launch_gemm_mfma(M, N, K, a, b, y, dt, ld_y, st));
   return from_hip(nvfp4::launch_gemm_generic(M, N, K, a, b, y, dt, ld_y, st));
 }

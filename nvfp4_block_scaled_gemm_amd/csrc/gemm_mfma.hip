@@ -40,7 +40,17 @@ typedef __attribute__((address_space(1))) void* gbl_void_ptr;
 constexpr int kBK = 128;        // K elements per stage
 constexpr int kRowBytes = 64;   // nibble bytes per row per stage
 constexpr int kScBytes = 8;     // scale bytes per row per stage
-constexpr int kStages = 3;      // LDS ring depth
+// Tuning knobs (compile-time): ring depth, row-swizzle shift, tile-row group.
+#ifndef NVFP4_MFMA_STAGES
+#define NVFP4_MFMA_STAGES 4
+#endif
+#ifndef NVFP4_MFMA_SWZ_SHIFT
+#define NVFP4_MFMA_SWZ_SHIFT 1
+#endif
+#ifndef NVFP4_MFMA_GROUP_M
+#define NVFP4_MFMA_GROUP_M 8
+#endif
+constexpr int kStages = NVFP4_MFMA_STAGES;  // LDS ring depth
 
 template <int BM, int BN>
 struct Smem {
@@ -52,7 +62,7 @@ struct Smem {
 };
 
 // 16-byte chunk swizzle of a 64-byte LDS row: physical chunk = logical ^ swz.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row >> NVFP4_MFMA_SWZ_SHIFT) & 3; }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -60,6 +70,11 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
 // Workgroup barrier that is also a compiler memory barrier, without the
@@ -72,7 +87,7 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   const int nt = tiles_m * tiles_n;
   int pid = blockIdx.x;
   if ((nt & 7) == 0) pid = (pid & 7) * (nt >> 3) + (pid >> 3);
-  constexpr int GROUP_M = 8;
+  constexpr int GROUP_M = NVFP4_MFMA_GROUP_M;
   const int per_group = GROUP_M * tiles_n;
   const int group = pid / per_group;
   const int first_m = group * GROUP_M;
@@ -82,47 +97,56 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gsz;
 }
 
-// 8 elements E2M1(nibble) * S from one packed dword, S a half of `sc`:
-// the hardware converts each byte into two fp16 (low nibble first) and one
-// packed multiply per pair applies S (selected half broadcast to both lanes).
-template <int HALF>
-__device__ __forceinline__ f16x8 dequant8(uint32_t packed, f16x2 sc) {
-  const f16x2 s2 = __builtin_shufflevector(sc, sc, HALF, HALF);
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 0) * s2;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 1) * s2;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2) * s2;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 3) * s2;
-  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
-                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
-                                 5, 6, 7);
-}
-
-// One wave-fragment of 32 rows for a stage: 32 nibble bytes + 4 scale bytes.
-struct Frag {
-  u32x4 lo, hi;    // dwords 0..3 and 4..7 (MFMA steps t = 0..7)
-  f16x2 s01, s23;  // E4M3 scales of the lane's 4 blocks as fp16 pairs
+// A wave's 32-row fragment of one stage, split by when it is consumed:
+// `lo` (MFMA steps 0-3) and `hi` (steps 4-7), 16 bytes each, plus the
+// lane's 4 E4M3 block scale bytes (converted to fp16 pairs only when first
+// needed, so the LDS read latency is never waited on).
+struct FragLo {
+  u32x4 d;
+  uint32_t s4;
 };
 
-__device__ __forceinline__ Frag read_frag(const uint8_t* nib, const uint8_t* sc, int row, int g) {
-  Frag f;
-  const int sw = swz(row);
-  f.lo = *reinterpret_cast<const u32x4*>(nib + row * kRowBytes + (((2 * g) ^ sw) << 4));
-  f.hi = *reinterpret_cast<const u32x4*>(nib + row * kRowBytes + (((2 * g + 1) ^ sw) << 4));
-  const uint32_t s4 = *reinterpret_cast<const uint32_t*>(sc + row * kScBytes + 4 * g);
-  f.s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, false);
-  f.s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, true);
+struct Scales {
+  f16x2 s01, s23;  // blocks 0,1 and 2,3 of the lane
+};
+
+__device__ __forceinline__ FragLo read_lo(const uint8_t* nib, const uint8_t* sc, int row, int g) {
+  FragLo f;
+  f.d = *reinterpret_cast<const u32x4*>(nib + row * kRowBytes + (((2 * g) ^ swz(row)) << 4));
+  f.s4 = *reinterpret_cast<const uint32_t*>(sc + row * kScBytes + 4 * g);
   return f;
 }
 
-template <int T>
-__device__ __forceinline__ f16x8 frag_step(const Frag& f) {
-  constexpr int D = T & 3;
-  const uint32_t w = (T < 4) ? f.lo[D] : f.hi[D];
-  // step T uses block T/2 of the lane: 0,1 -> s01, 2,3 -> s23
-  if constexpr ((T >> 1) == 0) return dequant8<0>(w, f.s01);
-  else if constexpr ((T >> 1) == 1) return dequant8<1>(w, f.s01);
-  else if constexpr ((T >> 1) == 2) return dequant8<0>(w, f.s23);
-  else return dequant8<1>(w, f.s23);
+__device__ __forceinline__ Scales to_scales(uint32_t s4) {
+  return {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, false),
+          __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, true)};
+}
+
+__device__ __forceinline__ u32x4 read_hi(const uint8_t* nib, int row, int g) {
+  return *reinterpret_cast<const u32x4*>(nib + row * kRowBytes + (((2 * g + 1) ^ swz(row)) << 4));
+}
+
+// Elements 4H .. 4H+3 of MFMA step T (8 elements of one block): one
+// conversion and one multiply per pair, written into `out`.
+template <int T, int H>
+__device__ __forceinline__ void dequant_piece(uint32_t w, f16x2 s01, f16x2 s23, f16x8& out) {
+  const f16x2 sc = ((T >> 1) < 2) ? s01 : s23;
+  constexpr int HALF = (T >> 1) & 1;
+  const f16x2 s2 = __builtin_shufflevector(sc, sc, HALF, HALF);
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H) * s2;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H + 1) * s2;
+  out[4 * H + 0] = p0[0];
+  out[4 * H + 1] = p0[1];
+  out[4 * H + 2] = p1[0];
+  out[4 * H + 3] = p1[1];
+}
+
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -141,15 +165,25 @@ struct Cfg {
                 "tile too small for the load split");
 };
 
+// Stage variants of the main loop (4-deep ring):
+//   kFull  - mid-stage sync waits for stage s+1 with one younger stage in
+//            flight, then refills the ring with stage s+3;
+//   kTail1 - same wait, nothing left to load;
+//   kTail0 - stage s+1 is the youngest load: wait for all;
+//   kLast  - no next stage.
+enum StageMode { kFull, kTail1, kTail0, kLast };
+
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
     int M, int N, int K, const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
     const float* __restrict__ a_g, const uint8_t* __restrict__ b_q,
     const uint8_t* __restrict__ b_s, const float* __restrict__ b_g, void* __restrict__ y,
     int y_dtype, int64_t ld_y) {
+  static_assert(kStages == 4, "stage modes assume a 4-deep ring");
   using C = Cfg<BM, BN, WAVES_M, WAVES_N>;
   using L = Smem<BM, BN>;
-  constexpr int FM = C::FM, FN = C::FN;
+  constexpr int FM = C::FM, FN = C::FN, NF = FM + FN, Q = FM * FN;
+  constexpr int P = 2 * NF;  // dequant pieces per MFMA step
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -159,67 +193,70 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   int tm, tn;
   tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int64_t rowq = K / 2, rows = K / 16;
+  const uint32_t rowq = (uint32_t)(K / 2), rows = (uint32_t)(K / 16);
   const int nstage = K / kBK;
 
-  // Per-lane source offsets (bytes, relative to the stage's column origin).
-  // Rows past M / N are clamped to the last valid row: they only feed outputs
-  // that are never stored.
-  int64_t a_nib_off[C::kANibLoads], b_nib_off[C::kBNibLoads];
-  int64_t a_sc_off[C::kAScLoads], b_sc_off[C::kBScLoads];
+  // Per-lane 32-bit source offsets (operands are < 4 GiB; checked by the
+  // launcher) relative to the stage's column origin.  Rows past M / N are
+  // clamped to the last valid row: they only feed outputs that are not stored.
+  uint32_t a_nib_off[C::kANibLoads], b_nib_off[C::kBNibLoads];
+  uint32_t a_sc_off[C::kAScLoads], b_sc_off[C::kBScLoads];
 #pragma unroll
   for (int i = 0; i < C::kANibLoads; ++i) {
     const int slot = (wave * C::kANibLoads + i) * 64 + lane;   // 16-byte LDS slot
     const int r = slot >> 2, phys = slot & 3;
-    const int gr = min(m0 + r, M - 1);
-    a_nib_off[i] = (int64_t)gr * rowq + ((phys ^ swz(r)) << 4);
+    a_nib_off[i] = (uint32_t)min(m0 + r, M - 1) * rowq + ((phys ^ swz(r)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < C::kBNibLoads; ++i) {
     const int slot = (wave * C::kBNibLoads + i) * 64 + lane;
     const int r = slot >> 2, phys = slot & 3;
-    const int gr = min(n0 + r, N - 1);
-    b_nib_off[i] = (int64_t)gr * rowq + ((phys ^ swz(r)) << 4);
+    b_nib_off[i] = (uint32_t)min(n0 + r, N - 1) * rowq + ((phys ^ swz(r)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < C::kAScLoads; ++i) {
     const int slot = (wave * C::kAScLoads + i) * 64 + lane;     // 4-byte LDS slot
-    const int gr = min(m0 + (slot >> 1), M - 1);
-    a_sc_off[i] = (int64_t)gr * rows + ((slot & 1) << 2);
+    a_sc_off[i] = (uint32_t)min(m0 + (slot >> 1), M - 1) * rows + ((slot & 1) << 2);
   }
 #pragma unroll
   for (int i = 0; i < C::kBScLoads; ++i) {
     const int slot = (wave * C::kBScLoads + i) * 64 + lane;
-    const int gr = min(n0 + (slot >> 1), N - 1);
-    b_sc_off[i] = (int64_t)gr * rows + ((slot & 1) << 2);
+    b_sc_off[i] = (uint32_t)min(n0 + (slot >> 1), N - 1) * rows + ((slot & 1) << 2);
   }
 
-  auto issue = [&](int st) {
-    uint8_t* base = smem + (st % kStages) * L::kBytes;
-    const uint8_t* aq = a_q + (int64_t)st * kRowBytes;
-    const uint8_t* bq = b_q + (int64_t)st * kRowBytes;
-    const uint8_t* as = a_s + (int64_t)st * kScBytes;
-    const uint8_t* bs = b_s + (int64_t)st * kScBytes;
-#pragma unroll
-    for (int i = 0; i < C::kANibLoads; ++i)
+  // Direct load number J (0 .. kLoads-1) of stage st into its ring buffer.
+  auto load_one = [&](int st, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    uint8_t* base = smem + (st & (kStages - 1)) * L::kBytes;
+    if constexpr (J < C::kANibLoads) {
       __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(aq + a_nib_off[i]),
-          (lds_void_ptr)(base + L::kANib + (wave * C::kANibLoads + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kBNibLoads; ++i)
+          (gbl_void_ptr)(a_q + (uint32_t)st * kRowBytes + a_nib_off[J]),
+          (lds_void_ptr)(base + L::kANib + (wave * C::kANibLoads + J) * 1024), 16, 0, 0);
+    } else if constexpr (J < C::kANibLoads + C::kBNibLoads) {
+      constexpr int i = J - C::kANibLoads;
       __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(bq + b_nib_off[i]),
+          (gbl_void_ptr)(b_q + (uint32_t)st * kRowBytes + b_nib_off[i]),
           (lds_void_ptr)(base + L::kBNib + (wave * C::kBNibLoads + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kAScLoads; ++i)
+    } else if constexpr (J < C::kANibLoads + C::kBNibLoads + C::kAScLoads) {
+      constexpr int i = J - C::kANibLoads - C::kBNibLoads;
       __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(as + a_sc_off[i]),
+          (gbl_void_ptr)(a_s + (uint32_t)st * kScBytes + a_sc_off[i]),
           (lds_void_ptr)(base + L::kASc + (wave * C::kAScLoads + i) * 256), 4, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kBScLoads; ++i)
+    } else {
+      constexpr int i = J - C::kANibLoads - C::kBNibLoads - C::kAScLoads;
       __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(bs + b_sc_off[i]),
+          (gbl_void_ptr)(b_s + (uint32_t)st * kScBytes + b_sc_off[i]),
           (lds_void_ptr)(base + L::kBSc + (wave * C::kBScLoads + i) * 256), 4, 0, 0);
+    }
+  };
+  auto issue = [&](int st) { static_for<C::kLoads>([&](auto jc) { load_one(st, jc); }); };
+
+  auto frag_row = [&](int f) { return f < FM ? wm * C::TM + f * 32 + li : wn * C::TN + (f - FM) * 32 + li; };
+  auto nib_base = [&](int st, int f) {
+    return smem + (st & (kStages - 1)) * L::kBytes + (f < FM ? L::kANib : L::kBNib);
+  };
+  auto sc_base = [&](int st, int f) {
+    return smem + (st & (kStages - 1)) * L::kBytes + (f < FM ? L::kASc : L::kBSc);
   };
 
   f32x16 acc[FM][FN];
@@ -228,52 +265,108 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  // prologue: stages 0 .. kStages-2 in flight
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nstage) issue(s);
+  FragLo lo[NF];
+  u32x4 hi[NF];
+  Scales sc[NF];
+  f16x8 cur[NF];
 
-  for (int st = 0; st < nstage; ++st) {
-    // this wave's loads of stage st have landed once at most the loads of the
-    // younger stages in flight remain; the barrier extends that to all waves
-    if (st + kStages - 2 < nstage) wait_vmcnt<(kStages - 2) * C::kLoads>();
-    else wait_vmcnt<0>();
-    workgroup_barrier();
-    // the buffer refilled here was last read in iteration st-1, which every
-    // wave has finished by the barrier above
-    if (st + kStages - 1 < nstage) issue(st + kStages - 1);
-
-    const uint8_t* base = smem + (st % kStages) * L::kBytes;
-    Frag fa[FM], fb[FN];
+  // ---- prologue: stages 0..2 in flight, stage 0 read, step 0 dequantised
 #pragma unroll
-    for (int f = 0; f < FM; ++f)
-      fa[f] = read_frag(base + L::kANib, base + L::kASc, wm * C::TM + f * 32 + li, lg);
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nstage) issue(st);
+  if (nstage >= 3) wait_vmcnt<2 * C::kLoads>();
+  else if (nstage == 2) wait_vmcnt<C::kLoads>();
+  else wait_vmcnt<0>();
+  workgroup_barrier();
 #pragma unroll
-    for (int f = 0; f < FN; ++f)
-      fb[f] = read_frag(base + L::kBNib, base + L::kBSc, wn * C::TN + f * 32 + li, lg);
-
-    auto step = [&](auto tc) {
-      constexpr int T = decltype(tc)::value;
-      f16x8 av[FM], bv[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) av[f] = frag_step<T>(fa[f]);
-#pragma unroll
-      for (int f = 0; f < FN; ++f) bv[f] = frag_step<T>(fb[f]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    };
-    step(std::integral_constant<int, 0>{});
-    step(std::integral_constant<int, 1>{});
-    step(std::integral_constant<int, 2>{});
-    step(std::integral_constant<int, 3>{});
-    step(std::integral_constant<int, 4>{});
-    step(std::integral_constant<int, 5>{});
-    step(std::integral_constant<int, 6>{});
-    step(std::integral_constant<int, 7>{});
+  for (int f = 0; f < NF; ++f) {
+    lo[f] = read_lo(nib_base(0, f), sc_base(0, f), frag_row(f), lg);
+    hi[f] = read_hi(nib_base(0, f), frag_row(f), lg);
   }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    sc[f] = to_scales(lo[f].s4);
+    dequant_piece<0, 0>(lo[f].d[0], sc[f].s01, sc[f].s23, cur[f]);
+    dequant_piece<0, 1>(lo[f].d[0], sc[f].s01, sc[f].s23, cur[f]);
+  }
+
+  // ---- one stage: 8 MFMA steps of FM x FN 32x32x16 MFMAs.  After each MFMA
+  // of step T go the dequant pieces of step T+1 (P pieces spread over the Q
+  // MFMAs), so the matrix core never waits on a long run of vector ops.
+  // Between steps 2 and 3 the workgroup syncs on stage s+1 (its `lo` halves
+  // are dead by then); step 3 reads them into registers and refills the ring;
+  // step 7 reads the `hi` halves of s+1 and dequantises its step 0.
+  auto run_stage = [&](int s, auto mc) {
+    constexpr StageMode MODE = decltype(mc)::value;
+    constexpr bool NEXT = MODE != kLast;
+    FragLo nlo[NF];
+    u32x4 nhi[NF];
+    Scales nsc[NF];
+    f16x8 nxt[NF];
+    static_for<8>([&](auto tc) {
+      constexpr int T = decltype(tc)::value;
+      if constexpr (T == 3 && NEXT) {
+        if constexpr (MODE == kTail0) wait_vmcnt<0>();
+        else wait_vmcnt<C::kLoads>();
+        workgroup_barrier();
+      }
+      static_for<Q>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        constexpr int i = I / FN, j = I % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[i], cur[FM + j], acc[i][j], 0, 0, 0);
+        // dequant pieces [I*P/Q, (I+1)*P/Q) of the next step
+        static_for<(I + 1) * P / Q - I * P / Q>([&](auto pc) {
+          constexpr int p = I * P / Q + decltype(pc)::value;
+          constexpr int F = p / 2, H = p % 2;
+          if constexpr (T < 3) {
+            dequant_piece<T + 1, H>(lo[F].d[T + 1], sc[F].s01, sc[F].s23, nxt[F]);
+          } else if constexpr (T < 7) {
+            dequant_piece<T + 1, H>(hi[F][T - 3], sc[F].s01, sc[F].s23, nxt[F]);
+          } else if constexpr (NEXT) {
+            if constexpr (H == 0) nsc[F] = to_scales(nlo[F].s4);
+            dequant_piece<0, H>(nlo[F].d[0], nsc[F].s01, nsc[F].s23, nxt[F]);
+          }
+        });
+        if constexpr (T == 3 && NEXT) {
+          // lo halves of stage s+1 into registers, then refill the ring
+          if constexpr (I < NF) nlo[I] = read_lo(nib_base(s + 1, I), sc_base(s + 1, I), frag_row(I), lg);
+          if constexpr (MODE == kFull) {
+            constexpr int J0 = I * C::kLoads / Q, J1 = (I + 1) * C::kLoads / Q;
+            static_for<J1 - J0>([&](auto jc) {
+              load_one(s + kStages - 1, std::integral_constant<int, J0 + decltype(jc)::value>{});
+            });
+          }
+        }
+        if constexpr (T == 7 && NEXT) {
+          if constexpr (I < NF) nhi[I] = read_hi(nib_base(s + 1, I), frag_row(I), lg);
+        }
+        // the hi reads of the previous stage finished long ago; saying so
+        // here keeps the compiler from waiting for them behind newer reads
+        if constexpr (T == 0 && I == 0) wait_lgkmcnt0();
+        // likewise for the lo reads of step 3, before step 7 issues new reads
+        if constexpr (T == 6 && I == 0 && NEXT) wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (T < 7 || NEXT) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
+      }
+    });
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        lo[f] = nlo[f];
+        hi[f] = nhi[f];
+        sc[f] = nsc[f];
+      }
+    }
+  };
+
+  int s = 0;
+  for (; s + kStages - 1 < nstage; ++s) run_stage(s, std::integral_constant<StageMode, kFull>{});
+  if (s + 2 < nstage) run_stage(s++, std::integral_constant<StageMode, kTail1>{});
+  if (s + 1 < nstage) run_stage(s++, std::integral_constant<StageMode, kTail0>{});
+  run_stage(s, std::integral_constant<StageMode, kLast>{});
 
   // ---- epilogue: y = fl32(ga * gb) * acc.  acc[i][j] reg r holds row
   // 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of its 32x32 tile.
