@@ -61,6 +61,13 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
+    # every host-side kernel stub must resolve: load the library once
+    # (no GPU needed; a silently dropped template stub fails here)
+    import ctypes
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as exc:
+        raise RuntimeError(f"built library does not load: {exc}") from exc
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

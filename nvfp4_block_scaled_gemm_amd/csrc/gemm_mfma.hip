@@ -35,7 +35,6 @@ namespace nvfp4 {
 namespace {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) void* gbl_void_ptr;
 
 constexpr int kBK = 128;        // K elements per stage
 constexpr int kRowBytes = 64;   // nibble bytes per row per stage
@@ -60,6 +59,23 @@ struct Smem {
   static constexpr int kBSc = kASc + BM * kScBytes;
   static constexpr int kBytes = kBSc + BN * kScBytes;  // one stage
 };
+
+// Direct buffer loads into LDS.  Each lane reads `size` bytes at
+// p + voff + soff (raw buffer, stride 0, range `bytes`: accesses past the end
+// read as zero) and the wave writes them to lds + lane * size.  The
+// descriptor is built from scalar values, so it stays in SGPRs.
+__device__ __forceinline__ void buffer_load_lds16(const void* p, uint32_t bytes, void* lds,
+                                                  uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000),
+      (lds_void_ptr)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(const void* p, uint32_t bytes, void* lds,
+                                                 uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000),
+      (lds_void_ptr)lds, 4, voff, soff, 0, 0);
+}
 
 // 16-byte chunk swizzle of a 64-byte LDS row: physical chunk = logical ^ swz.
 __device__ __forceinline__ int swz(int row) { return (row >> NVFP4_MFMA_SWZ_SHIFT) & 3; }
@@ -186,7 +202,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   constexpr int P = 2 * NF;  // dequant pieces per MFMA step
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar, so LDS destinations (M0) are scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int li = lane & 31, lg = lane >> 5;
 
@@ -224,29 +242,32 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
     b_sc_off[i] = (uint32_t)min(n0 + (slot >> 1), N - 1) * rows + ((slot & 1) << 2);
   }
 
+  // Byte ranges of the four operand arrays (< 4 GiB, checked by the launcher).
+  // The per-lane offsets above stay in VGPRs for the whole kernel and the
+  // stage's column offset is a scalar operand, so a direct load costs no
+  // vector instructions.
+  const uint32_t aq_bytes = (uint32_t)M * rowq, bq_bytes = (uint32_t)N * rowq;
+  const uint32_t as_bytes = (uint32_t)M * rows, bs_bytes = (uint32_t)N * rows;
+
   // Direct load number J (0 .. kLoads-1) of stage st into its ring buffer.
   auto load_one = [&](int st, auto jc) {
     constexpr int J = decltype(jc)::value;
     uint8_t* base = smem + (st & (kStages - 1)) * L::kBytes;
     if constexpr (J < C::kANibLoads) {
-      __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(a_q + (uint32_t)st * kRowBytes + a_nib_off[J]),
-          (lds_void_ptr)(base + L::kANib + (wave * C::kANibLoads + J) * 1024), 16, 0, 0);
+      buffer_load_lds16(a_q, aq_bytes, base + L::kANib + (wave * C::kANibLoads + J) * 1024,
+                        a_nib_off[J], (uint32_t)st * kRowBytes);
     } else if constexpr (J < C::kANibLoads + C::kBNibLoads) {
       constexpr int i = J - C::kANibLoads;
-      __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(b_q + (uint32_t)st * kRowBytes + b_nib_off[i]),
-          (lds_void_ptr)(base + L::kBNib + (wave * C::kBNibLoads + i) * 1024), 16, 0, 0);
+      buffer_load_lds16(b_q, bq_bytes, base + L::kBNib + (wave * C::kBNibLoads + i) * 1024,
+                        b_nib_off[i], (uint32_t)st * kRowBytes);
     } else if constexpr (J < C::kANibLoads + C::kBNibLoads + C::kAScLoads) {
       constexpr int i = J - C::kANibLoads - C::kBNibLoads;
-      __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(a_s + (uint32_t)st * kScBytes + a_sc_off[i]),
-          (lds_void_ptr)(base + L::kASc + (wave * C::kAScLoads + i) * 256), 4, 0, 0);
+      buffer_load_lds4(a_s, as_bytes, base + L::kASc + (wave * C::kAScLoads + i) * 256,
+                       a_sc_off[i], (uint32_t)st * kScBytes);
     } else {
       constexpr int i = J - C::kANibLoads - C::kBNibLoads - C::kAScLoads;
-      __builtin_amdgcn_global_load_lds(
-          (gbl_void_ptr)(b_s + (uint32_t)st * kScBytes + b_sc_off[i]),
-          (lds_void_ptr)(base + L::kBSc + (wave * C::kBScLoads + i) * 256), 4, 0, 0);
+      buffer_load_lds4(b_s, bs_bytes, base + L::kBSc + (wave * C::kBScLoads + i) * 256,
+                       b_sc_off[i], (uint32_t)st * kScBytes);
     }
   };
   auto issue = [&](int st) { static_for<C::kLoads>([&](auto jc) { load_one(st, jc); }); };
@@ -327,15 +348,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
             dequant_piece<0, H>(nlo[F].d[0], nsc[F].s01, nsc[F].s23, nxt[F]);
           }
         });
-        if constexpr (T == 3 && NEXT) {
-          // lo halves of stage s+1 into registers, then refill the ring
-          if constexpr (I < NF) nlo[I] = read_lo(nib_base(s + 1, I), sc_base(s + 1, I), frag_row(I), lg);
-          if constexpr (MODE == kFull) {
-            constexpr int J0 = I * C::kLoads / Q, J1 = (I + 1) * C::kLoads / Q;
-            static_for<J1 - J0>([&](auto jc) {
-              load_one(s + kStages - 1, std::integral_constant<int, J0 + decltype(jc)::value>{});
-            });
-          }
+        if constexpr ((T == 3 || T == 4) && NEXT) {
+          // lo halves of stage s+1 into registers, one fragment every other
+          // MFMA of steps 3 and 4
+          constexpr int SL = (T - 3) * Q + I;
+          if constexpr (SL % 2 == 0 && SL / 2 < NF)
+            nlo[SL / 2] = read_lo(nib_base(s + 1, SL / 2), sc_base(s + 1, SL / 2), frag_row(SL / 2), lg);
+        }
+        if constexpr (T >= 3 && T <= 6 && MODE == kFull) {
+          // refill the ring: the kLoads direct loads spread over steps 3-6
+          constexpr int SL = (T - 3) * Q + I, NS = 4 * Q;
+          constexpr int J0 = SL * C::kLoads / NS, J1 = (SL + 1) * C::kLoads / NS;
+          static_for<J1 - J0>([&](auto jc) {
+            load_one(s + kStages - 1, std::integral_constant<int, J0 + decltype(jc)::value>{});
+          });
         }
         if constexpr (T == 7 && NEXT) {
           if constexpr (I < NF) nhi[I] = read_hi(nib_base(s + 1, I), frag_row(I), lg);
