@@ -15,8 +15,9 @@ Prints one JSON line.  ``value`` is 2*M*N*K flop per step / step time
 ``roofline`` describes the GEMM kernel alone: algorithmic flop per launch
 over its average launch time (HIP events on the launch stream) against the
 fp16 dense matrix-core peak, since that is the MFMA family the kernel
-issues.  ``decode_m16`` is the skinny M=16 GEMM over 16 rotating copies of W
-(604 MB, so the 256 MB Infinity Cache cannot hold them), against HBM peak.
+issues.  ``decode`` holds the skinny M = 1, 16, 32 GEMMs over 16 rotating copies of W
+(604 MB, so the 256 MB Infinity Cache cannot hold them) and ``moe_grouped``
+the two grouped expert GEMMs, each against HBM peak.
 ``cpu_baseline`` times the CPU oracle on a bounded row slice of the same step.
 """
 from __future__ import annotations
@@ -151,25 +152,69 @@ def main():
     value = flop / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flop / (gemm_ms * 1e-3) / 1e12
 
-    # skinny decode M=16 over rotating weight copies (cache-cold W)
-    dcfg = wl.DECODE[16]
-    xd = nv.nvfp4_quantize(wl.randn((16, dcfg.K), wl.seed_for(2, 0), "bf16").to(dev))
+    # skinny decode GEMMs (M = 1, 16, 32) over 16 rotating weight copies
+    # (604 MB, more than the 256 MB Infinity Cache holds: cache-cold W)
     copies = [tuple(t.clone() for t in wq) for _ in range(16)]
-    yd = torch.empty((16, dcfg.N), dtype=torch.bfloat16, device=dev)
-    for c in copies:
-        nv.nvfp4_gemm(xd, c, "bf16", y=yd)
-    reps = 8
-    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps * len(copies))]
-    torch.cuda.synchronize()
-    for i in range(reps * len(copies)):
-        dev_ev[i][0].record(stream)
-        nv.nvfp4_gemm(xd, copies[i % len(copies)], "bf16", y=yd)
-        dev_ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = sum(a.elapsed_time(b) for a, b in dev_ev) / len(dev_ev)
-    dec_bytes = (dcfg.N * dcfg.K * 9 // 16) + (16 * dcfg.K * 9 // 16) + 16 * dcfg.N * 2
-    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+    decode = {}
+    for m in (1, 16, 32):
+        dcfg = wl.DECODE[m]
+        xd = nv.nvfp4_quantize(wl.randn((m, dcfg.K), wl.seed_for(2, 0), "bf16").to(dev))
+        yd = torch.empty((m, dcfg.N), dtype=torch.bfloat16, device=dev)
+        timed(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 16)
+        ms = timed(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 128)
+        nbytes = dcfg.N * dcfg.K * 9 // 16 + m * dcfg.K * 9 // 16 + m * dcfg.N * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        decode[f"m{m}"] = {"us": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
+                           "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                           "tflops": round(2.0 * m * dcfg.N * dcfg.K / (ms * 1e-3) / 1e12, 3)}
+    del copies
+
+    # MoE grouped GEMMs: 512 tokens, top-8 of 256 experts (seeded softmax
+    # router); gate_up N=4096 K=6144 then down N=6144 K=2048 (independent
+    # inputs).  3.6 + 1.8 GB of packed expert weights: cache-cold by size.
+    routing = wl.moe_routing(wl.seed_for(3, 0))
+    off = routing.m_offsets.to(dev)
+    total = int(routing.m_offsets[-1])
+    moe = {"tokens": wl.MOE_TOKENS, "experts": wl.MOE_EXPERTS, "topk": wl.MOE_TOPK,
+           "rows_per_expert_min": int(routing.counts.min()),
+           "rows_per_expert_max": int(routing.counts.max())}
+    for proj, (n_, k_) in (("gate_up", wl.MOE_GATE_UP), ("down", wl.MOE_DOWN)):
+        E = wl.MOE_EXPERTS
+        bq = torch.empty((E, n_, k_ // 2), dtype=torch.uint8, device=dev)
+        bs = torch.empty((E, n_, k_ // 16), dtype=torch.uint8, device=dev)
+        bg = torch.empty((E,), dtype=torch.float32, device=dev)
+        for e in range(E):
+            we = wl.randn((n_, k_), wl.seed_for(3, (100 if proj == "gate_up" else 1000) + e),
+                          "bf16", device=dev)
+            nv.nvfp4_quantize(we, out=(bq[e], bs[e], bg[e:e + 1]))
+        del we
+        if proj == "gate_up":
+            xq = nv.nvfp4_quantize(wl.randn((wl.MOE_TOKENS, k_), wl.seed_for(3, 1), "bf16").to(dev))
+            rt = routing.row_token.to(dev)
+            a = (xq[0].index_select(0, rt), xq[1].index_select(0, rt), xq[2])
+        else:
+            a = nv.nvfp4_quantize(wl.randn((total, k_), wl.seed_for(3, 2), "bf16").to(dev))
+        ym = torch.empty((total, n_), dtype=torch.bfloat16, device=dev)
+        timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 3)
+        ms = timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 10)
+        nbytes = E * n_ * k_ * 9 // 16 + total * k_ * 9 // 16 + total * n_ * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        moe[proj] = {"N": n_, "K": k_, "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+                     "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "tflops": round(2.0 * total * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
+        del bq, bs, bg, a, ym
 
     out = {
         "metric": "NVFP4 GEMM TFLOPS + % of MFMA/HBM roofline (M=4096,N=K=8192; M=16 decode)",
@@ -192,11 +237,9 @@ def main():
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": measured_traffic()},
-        "decode_m16": {"workload": dcfg.name, "us": round(dec_ms * 1e3, 3),
-                       "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbs, 1),
-                       "peak_GBps": PEAK_HBM_GBS, "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                       "tflops": round(2.0 * 16 * dcfg.N * dcfg.K / (dec_ms * 1e-3) / 1e12, 3),
-                       "weights": "16 rotating copies (cache-cold)"},
+        "decode": dict(decode, workload="decode_m{1,16,32}_n8192_k8192", peak_GBps=PEAK_HBM_GBS,
+                       weights="16 rotating copies (cache-cold)"),
+        "moe_grouped": dict(moe, peak_GBps=PEAK_HBM_GBS),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, args.cpu_rows)

@@ -28,7 +28,7 @@ bool tiled_ok(int64_t K, const uint8_t* q, const uint8_t* s, int64_t kmult) {
 }
 
 // The MFMA tile kernel addresses each operand with 32-bit byte offsets.
-bool offsets32_ok(int64_t rows, int64_t K) { return rows * (K / 2) < ((int64_t)1 << 32); }
+bool offsets32_ok(int64_t rows, int64_t K) { return (rows + 32) * (K / 2) < ((int64_t)1 << 32) - 16; }
 
 }  // namespace
 
@@ -111,7 +111,8 @@ int nvfp4_grouped_gemm(int32_t G, const int32_t* m_offsets, int64_t total_m, int
     return NVFP4_ERR_INVALID_ARG;
   const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
   hipStream_t st = (hipStream_t)stream;
-  if (K > 0 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256))
+  if (K > 0 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256) &&
+      offsets32_ok(total_m, K) && offsets32_ok(N, K))
     return from_hip(nvfp4::launch_gemm_grouped(G, m_offsets, total_m, N, K, a, b, y,
                                                (int)y_dtype, ld_y, st));
   return from_hip(nvfp4::launch_gemm_grouped_generic(G, m_offsets, total_m, N, K, a, b, y,

@@ -26,8 +26,6 @@
 //  * Workgroup ids are regrouped XCD-aware: hardware ids go round-robin over
 //    the 8 XCDs, so each XCD is given a compact block of output tiles whose
 //    A and B rows it shares in its own L2.
-#include <type_traits>
-
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -122,10 +120,6 @@ struct FragLo {
   uint32_t s4;
 };
 
-struct Scales {
-  f16x2 s01, s23;  // blocks 0,1 and 2,3 of the lane
-};
-
 __device__ __forceinline__ FragLo read_lo(const uint8_t* nib, const uint8_t* sc, int row, int g) {
   FragLo f;
   f.d = *reinterpret_cast<const u32x4*>(nib + row * kRowBytes + (((2 * g) ^ swz(row)) << 4));
@@ -133,36 +127,8 @@ __device__ __forceinline__ FragLo read_lo(const uint8_t* nib, const uint8_t* sc,
   return f;
 }
 
-__device__ __forceinline__ Scales to_scales(uint32_t s4) {
-  return {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, false),
-          __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, true)};
-}
-
 __device__ __forceinline__ u32x4 read_hi(const uint8_t* nib, int row, int g) {
   return *reinterpret_cast<const u32x4*>(nib + row * kRowBytes + (((2 * g + 1) ^ swz(row)) << 4));
-}
-
-// Elements 4H .. 4H+3 of MFMA step T (8 elements of one block): one
-// conversion and one multiply per pair, written into `out`.
-template <int T, int H>
-__device__ __forceinline__ void dequant_piece(uint32_t w, f16x2 s01, f16x2 s23, f16x8& out) {
-  const f16x2 sc = ((T >> 1) < 2) ? s01 : s23;
-  constexpr int HALF = (T >> 1) & 1;
-  const f16x2 s2 = __builtin_shufflevector(sc, sc, HALF, HALF);
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H) * s2;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H + 1) * s2;
-  out[4 * H + 0] = p0[0];
-  out[4 * H + 1] = p0[1];
-  out[4 * H + 2] = p1[0];
-  out[4 * H + 3] = p1[1];
-}
-
-template <int N, typename F, int I = 0>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, F, I + 1>(static_cast<F&&>(f));
-  }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -307,8 +273,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     sc[f] = to_scales(lo[f].s4);
-    dequant_piece<0, 0>(lo[f].d[0], sc[f].s01, sc[f].s23, cur[f]);
-    dequant_piece<0, 1>(lo[f].d[0], sc[f].s01, sc[f].s23, cur[f]);
+    dequant_piece<0, 0>(lo[f].d[0], sc[f], cur[f]);
+    dequant_piece<0, 1>(lo[f].d[0], sc[f], cur[f]);
   }
 
   // ---- one stage: 8 MFMA steps of FM x FN 32x32x16 MFMAs.  After each MFMA
@@ -340,12 +306,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
           constexpr int p = I * P / Q + decltype(pc)::value;
           constexpr int F = p / 2, H = p % 2;
           if constexpr (T < 3) {
-            dequant_piece<T + 1, H>(lo[F].d[T + 1], sc[F].s01, sc[F].s23, nxt[F]);
+            dequant_piece<T + 1, H>(lo[F].d[T + 1], sc[F], nxt[F]);
           } else if constexpr (T < 7) {
-            dequant_piece<T + 1, H>(hi[F][T - 3], sc[F].s01, sc[F].s23, nxt[F]);
+            dequant_piece<T + 1, H>(hi[F][T - 3], sc[F], nxt[F]);
           } else if constexpr (NEXT) {
             if constexpr (H == 0) nsc[F] = to_scales(nlo[F].s4);
-            dequant_piece<0, H>(nlo[F].d[0], nsc[F].s01, nsc[F].s23, nxt[F]);
+            dequant_piece<0, H>(nlo[F].d[0], nsc[F], nxt[F]);
           }
         });
         if constexpr ((T == 3 || T == 4) && NEXT) {

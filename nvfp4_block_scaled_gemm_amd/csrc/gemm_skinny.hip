@@ -12,10 +12,11 @@
 // bytes in flight as possible:
 //
 //  * One workgroup owns 32 weight rows (an n-tile) of one group over all of
-//    K.  Its 8 waves split K in units of 256 elements; per unit a lane loads
+//    K.  Its 8 waves split K in units of 256 elements; per unit a lane holds
 //    32 contiguous nibble bytes and 4 scale bytes of each of its two weight
-//    rows, so four lanes cover a full 128-byte line of a row.  All of a
-//    wave's units are loaded before the first is used.
+//    rows, so four lanes cover a full 128-byte line of a row.  Every weight
+//    and activation load of a wave (up to 4 units each) is issued before the
+//    first is used, so a CU has its whole weight slice in flight at once.
 //  * Products run on v_mfma_f32_16x16x32_f16 with weights as the 16-row A
 //    operand and up to 32 tokens as one or two B operands; both sides are
 //    dequantised exactly to fp16 in registers.  K is permuted identically on
@@ -35,10 +36,10 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWG = 32;   // weight rows (output columns) per workgroup
 constexpr int kUnitK = 256;      // K elements per wave step
-constexpr int kMaxUnits = 4;     // units held in registers per wave (K <= 8192 per round)
+constexpr int kMaxUnits = 4;     // units per wave per round (K <= 8192 per round)
 
 struct Unit {
-  u32x4 q0, q1;  // 32 nibble bytes = 64 elements
+  u32x4 q0, q1;  // 32 nibble bytes = 64 elements (MFMA steps 0-3, 4-7)
   uint32_t s;    // 4 scale bytes
 };
 
@@ -58,11 +59,67 @@ __device__ __forceinline__ Unit load_unit(const uint8_t* q_row, const uint8_t* s
   return r;
 }
 
-__device__ __forceinline__ uint32_t unit_word(const Unit& u, int t) {
-  return t < 4 ? u.q0[t] : u.q1[t - 4];
+template <int T>
+__device__ __forceinline__ uint32_t unit_word(const Unit& u) {
+  if constexpr (T < 4) return u.q0[T];
+  else return u.q1[T - 4];
 }
 
-// One 32-row x (<= 32 token) tile over all of K.
+struct Rows {
+  const uint8_t *q0, *q1, *s0, *s1;  // two rows (fragments 0 and 1) of one operand
+  bool v0, v1;
+};
+
+// One token chunk (<= 16 * NX tokens) of the 32-row tile, over all of K;
+// leaves the wave's partial sums in acc[f][g] (weight fragment f, token
+// fragment g).
+template <int NX>
+__device__ __forceinline__ void chunk_partial(const Rows& w, const Rows& x, int nunits, int wave,
+                                              int lq, f32x4 (&acc)[2][2]) {
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[f][g] = f32x4{0, 0, 0, 0};
+  for (int ub = wave; ub < nunits; ub += kWaves * kMaxUnits) {
+    Unit w0[kMaxUnits], w1[kMaxUnits], x0[kMaxUnits], x1[kMaxUnits];
+    // every load of the round first: weights, then activations
+#pragma unroll
+    for (int i = 0; i < kMaxUnits; ++i) {
+      const int u = ub + i * kWaves;
+      const bool in = u < nunits;
+      w0[i] = load_unit(w.q0, w.s0, u, lq, in && w.v0);
+      w1[i] = load_unit(w.q1, w.s1, u, lq, in && w.v1);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxUnits; ++i) {
+      const int u = ub + i * kWaves;
+      const bool in = u < nunits;
+      x0[i] = load_unit(x.q0, x.s0, u, lq, in && x.v0);
+      if constexpr (NX == 2) x1[i] = load_unit(x.q1, x.s1, u, lq, in && x.v1);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxUnits; ++i) {
+      if (ub + i * kWaves >= nunits) break;
+      const Scales sw0 = to_scales(w0[i].s), sw1 = to_scales(w1[i].s), sx0 = to_scales(x0[i].s);
+      Scales sx1;
+      if constexpr (NX == 2) sx1 = to_scales(x1[i].s);
+      static_for<8>([&](auto tc) {
+        constexpr int T = decltype(tc)::value;
+        const f16x8 a0 = dequant_step<T>(unit_word<T>(w0[i]), sw0);
+        const f16x8 a1 = dequant_step<T>(unit_word<T>(w1[i]), sw1);
+        const f16x8 b0 = dequant_step<T>(unit_word<T>(x0[i]), sx0);
+        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[0][0], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b0, acc[1][0], 0, 0, 0);
+        if constexpr (NX == 2) {
+          const f16x8 b1 = dequant_step<T>(unit_word<T>(x1[i]), sx1);
+          acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b1, acc[0][1], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[1][1], 0, 0, 0);
+        }
+      });
+    }
+  }
+}
+
 template <bool GROUPED>
 __global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(
     int N, int K, int tiles_per_group, const int32_t* __restrict__ m_offsets, int64_t total_m,
@@ -72,7 +129,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(
     int y_dtype, int64_t ld_y) {
   __shared__ float red[kWaves][kRowsPerWG][32 + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
   const int e = GROUPED ? (int)(blockIdx.x / tiles_per_group) : 0;
   const int nt = GROUPED ? (int)(blockIdx.x % tiles_per_group) : (int)blockIdx.x;
@@ -95,68 +153,39 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(
   const float alpha = a_g[0] * b_g[e];
 
   // weight rows of this lane: n0 + 16*f + li, f = 0, 1
-  const int wrow0 = n0 + li, wrow1 = n0 + 16 + li;
-  const bool wv0 = wrow0 < N, wv1 = wrow1 < N;
-  const uint8_t* wq0 = bq + (int64_t)wrow0 * qstride;
-  const uint8_t* wq1 = bq + (int64_t)wrow1 * qstride;
-  const uint8_t* ws0 = bs + (int64_t)wrow0 * sstride;
-  const uint8_t* ws1 = bs + (int64_t)wrow1 * sstride;
+  Rows w;
+  {
+    const int r0 = n0 + li, r1 = n0 + 16 + li;
+    w.v0 = r0 < N;
+    w.v1 = r1 < N;
+    w.q0 = bq + (int64_t)r0 * qstride;
+    w.q1 = bq + (int64_t)r1 * qstride;
+    w.s0 = bs + (int64_t)r0 * sstride;
+    w.s1 = bs + (int64_t)r1 * sstride;
+  }
 
   for (int64_t c0 = row_begin; c0 < row_end; c0 += 32) {
     const int ntok = (int)((row_end - c0) < 32 ? (row_end - c0) : 32);
-    const bool two = ntok > 16;  // wave-uniform
-    const int64_t xr0 = c0 + li, xr1 = c0 + 16 + li;
-    const bool xv0 = li < ntok, xv1 = 16 + li < ntok;
-    const uint8_t* xq0 = a_q + xr0 * qstride;
-    const uint8_t* xq1 = a_q + xr1 * qstride;
-    const uint8_t* xs0 = a_s + xr0 * sstride;
-    const uint8_t* xs1 = a_s + xr1 * sstride;
+    Rows x;
+    x.v0 = li < ntok;
+    x.v1 = 16 + li < ntok;
+    x.q0 = a_q + (c0 + li) * qstride;
+    x.q1 = a_q + (c0 + 16 + li) * qstride;
+    x.s0 = a_s + (c0 + li) * sstride;
+    x.s1 = a_s + (c0 + 16 + li) * sstride;
 
-    f32x4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc10 = {0, 0, 0, 0},
-          acc11 = {0, 0, 0, 0};
+    f32x4 acc[2][2];
+    if (ntok > 16) chunk_partial<2>(w, x, nunits, wave, lq, acc);  // wave-uniform
+    else chunk_partial<1>(w, x, nunits, wave, lq, acc);
 
-    for (int ub = wave; ub < nunits; ub += kWaves * kMaxUnits) {
-      // issue every weight load of this round first
-      Unit w0[kMaxUnits], w1[kMaxUnits];
+    // partial tiles -> LDS: acc[f][g] reg r is weight row 16f + 4*lq + r,
+    // token 16g + li
 #pragma unroll
-      for (int i = 0; i < kMaxUnits; ++i) {
-        const int u = ub + i * kWaves;
-        const bool in = u < nunits;
-        w0[i] = load_unit(wq0, ws0, u, lq, in && wv0);
-        w1[i] = load_unit(wq1, ws1, u, lq, in && wv1);
-      }
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int i = 0; i < kMaxUnits; ++i) {
-        const int u = ub + i * kWaves;
-        if (u >= nunits) break;
-        const Unit x0 = load_unit(xq0, xs0, u, lq, xv0);
-        Unit x1;
-        if (two) x1 = load_unit(xq1, xs1, u, lq, xv1);
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int sh = 8 * (t >> 1);
-          const f16x8 fw0 = dequant8_scaled(unit_word(w0[i], t), scale_pair_bits((w0[i].s >> sh) & 0xFFu));
-          const f16x8 fw1 = dequant8_scaled(unit_word(w1[i], t), scale_pair_bits((w1[i].s >> sh) & 0xFFu));
-          const f16x8 fx0 = dequant8_scaled(unit_word(x0, t), scale_pair_bits((x0.s >> sh) & 0xFFu));
-          acc00 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw0, fx0, acc00, 0, 0, 0);
-          acc10 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw1, fx0, acc10, 0, 0, 0);
-          if (two) {
-            const f16x8 fx1 = dequant8_scaled(unit_word(x1, t), scale_pair_bits((x1.s >> sh) & 0xFFu));
-            acc01 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw0, fx1, acc01, 0, 0, 0);
-            acc11 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw1, fx1, acc11, 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    // partial tiles -> LDS: acc[f][g] reg r is weight row 16f + 4*lq + r, token 16g + li
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      red[wave][4 * lq + r][li] = acc00[r];
-      red[wave][16 + 4 * lq + r][li] = acc10[r];
-      red[wave][4 * lq + r][16 + li] = acc01[r];
-      red[wave][16 + 4 * lq + r][16 + li] = acc11[r];
-    }
+        for (int r = 0; r < 4; ++r) red[wave][16 * f + 4 * lq + r][16 * g + li] = acc[f][g][r];
     __syncthreads();
     // 1024 outputs (32 tokens x 32 weight rows), two per thread, summed over
     // the waves in a fixed order
@@ -166,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(
       const int tok = o >> 5, wr = o & 31;
       float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += red[w][wr][tok];
+      for (int v = 0; v < kWaves; ++v) s += red[v][wr][tok];
       const int n = n0 + wr;
       if (tok < ntok && n < N) store_out(y, (c0 + tok) * ld_y + n, s * alpha, y_dtype);
     }
@@ -181,18 +210,6 @@ hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a, 
   const int64_t tiles = (N + kRowsPerWG - 1) / kRowsPerWG;
   gemm_skinny_kernel<false><<<(unsigned)tiles, kThreads, 0, stream>>>(
       (int)N, (int)K, (int)tiles, nullptr, M, a.q, a.s, a.g, b.q, b.s, b.g, y, y_dtype, ld_y);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, int64_t total_m, int64_t N,
-                               int64_t K, PackedOperand a, PackedOperand b, void* y, int y_dtype,
-                               int64_t ld_y, hipStream_t stream) {
-  const int64_t tiles = (N + kRowsPerWG - 1) / kRowsPerWG;
-  const int64_t grid = tiles * G;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  gemm_skinny_kernel<true><<<(unsigned)grid, kThreads, 0, stream>>>(
-      (int)N, (int)K, (int)tiles, m_offsets, total_m, a.q, a.s, a.g, b.q, b.s, b.g, y, y_dtype,
-      ld_y);
   return hipGetLastError();
 }
 

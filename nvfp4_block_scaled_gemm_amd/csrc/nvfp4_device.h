@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nvfp4 {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -30,30 +32,50 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
 }
 
-// {S, S} as fp16 bits with S = E4M3(byte) * 2^-8: E4M3 and fp16 share the
-// subnormal/normal structure, so the 7 magnitude bits shifted left by 7 are
-// exactly E4M3 * 2^-8 in fp16 (possibly subnormal); the sign moves to bit 15.
-// The factor 2^8 is restored by converting nibbles with a scale of 256.
-__device__ __forceinline__ uint32_t scale_pair_bits(uint32_t byte) {
-  const uint32_t h = ((byte & 0x7Fu) << 7) | ((byte & 0x80u) << 8);
-  return h | (h << 16);
+// The four E4M3 scale bytes of a lane's 64 K-elements as two fp16 pairs
+// (blocks 0,1 and 2,3), from the hardware FP8 pair conversion (exact: every
+// E4M3 value is an fp16 value).
+struct Scales {
+  f16x2 s01, s23;
+};
+
+__device__ __forceinline__ Scales to_scales(uint32_t s4) {
+  return {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, false),
+          __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, true)};
 }
 
-__device__ __forceinline__ f16x8 dequant8_scaled(uint32_t packed, uint32_t pair_bits) {
-  f16x2 s2;
-  __builtin_memcpy(&s2, &pair_bits, 4);
-  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 0);
-  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 1);
-  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 2);
-  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 256.0f, 3);
-  p0 *= s2;
-  p1 *= s2;
-  p2 *= s2;
-  p3 *= s2;
-  f16x8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+// Elements 4H .. 4H+3 of MFMA step T: a lane holds 64 consecutive K-elements
+// as 8 packed dwords (step T uses dword T, i.e. block T/2 of the lane).  The
+// hardware converts each byte into two fp16 (low nibble first, unit scale)
+// and one packed multiply per pair applies the block's E4M3 scale (the
+// selected half broadcast to both lanes).
+template <int T, int H>
+__device__ __forceinline__ void dequant_piece(uint32_t w, const Scales& sc, f16x8& out) {
+  const f16x2 s = ((T >> 1) < 2) ? sc.s01 : sc.s23;
+  constexpr int HALF = (T >> 1) & 1;
+  const f16x2 s2 = __builtin_shufflevector(s, s, HALF, HALF);
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H) * s2;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H + 1) * s2;
+  out[4 * H + 0] = p0[0];
+  out[4 * H + 1] = p0[1];
+  out[4 * H + 2] = p1[0];
+  out[4 * H + 3] = p1[1];
+}
+
+template <int T>
+__device__ __forceinline__ f16x8 dequant_step(uint32_t w, const Scales& sc) {
+  f16x8 out;
+  dequant_piece<T, 0>(w, sc, out);
+  dequant_piece<T, 1>(w, sc, out);
+  return out;
+}
+
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
