@@ -207,8 +207,8 @@ def main():
         else:
             a = nv.nvfp4_quantize(wl.randn((total, k_), wl.seed_for(3, 2), "bf16").to(dev))
         ym = torch.empty((total, n_), dtype=torch.bfloat16, device=dev)
-        timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 3)
-        ms = timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 10)
+        timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 10)
+        ms = timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 20)
         nbytes = E * n_ * k_ * 9 // 16 + total * k_ * 9 // 16 + total * n_ * 2
         gbs = nbytes / (ms * 1e-3) / 1e9
         moe[proj] = {"N": n_, "K": k_, "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,

@@ -111,7 +111,7 @@ int nvfp4_grouped_gemm(int32_t G, const int32_t* m_offsets, int64_t total_m, int
     return NVFP4_ERR_INVALID_ARG;
   const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
   hipStream_t st = (hipStream_t)stream;
-  if (K > 0 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256) &&
+  if (K > 0 && tiled_ok(K, a_q, a_s, 512) && tiled_ok(K, b_q, b_s, 512) &&
       offsets32_ok(total_m, K) && offsets32_ok(N, K))
     return from_hip(nvfp4::launch_gemm_grouped(G, m_offsets, total_m, N, K, a, b, y,
                                                (int)y_dtype, ld_y, st));

@@ -10,23 +10,31 @@
 // work hidden under it.
 //
 // Design (persistent, barrier-free):
-//  * Work items are (expert e, 32-row weight tile); a wave owns an item over
+//  * Work items are (expert e, 64-row weight tile); a wave owns an item over
 //    all of K and all of the expert's tokens, so no partial sums ever cross
 //    waves.  The waves of the grid walk the item list with a fixed stride;
-//    experts without tokens are skipped.
-//  * A wave's jobs are (item, 32-token chunk, 256-element K unit).  Each job
-//    brings 4.5 KB of packed weights into a private 3-slot LDS ring with
-//    buffer-to-LDS loads (4 x 16 B + 2 x 4 B per lane) and the chunk's
-//    activation fragments into registers with buffer loads; out-of-range rows
-//    read as zero.  Loads run two jobs ahead and every job issues the same 12
-//    memory instructions (finished items pad with out-of-range loads), so one
-//    fixed s_waitcnt per job suffices.
+//    experts without tokens are skipped.  One workgroup of four waves per CU
+//    (one wave per SIMD) leaves the whole LDS to the weight rings.
+//  * A wave's jobs are (item, 32-token chunk, 512-element K slice).  Lane
+//    group q of a job owns the slice's K-elements [128q, 128q+128), so every
+//    lane moves at least 8 contiguous bytes per load (loads of 4 bytes per
+//    lane cost nearly as much memory-pipeline time as 16-byte ones).  A job
+//    brings 18 KB of packed weights (64 rows x 256 B of nibbles + 32 B of
+//    scales) into a private 2-slot LDS ring with 16-byte buffer-to-LDS loads,
+//    and the chunk's activations (64 B of nibbles + 8 B of scales per lane
+//    and token fragment) into registers.  Rows past the operands read as
+//    zero; token rows outside the expert's chunk are not fetched.  Loads run
+//    one job ahead and every job issues the same 28 memory instructions (a
+//    finished wave pads with harmless reloads), so one fixed s_waitcnt per
+//    job suffices.  Weight rows are XOR-swizzled in 16-byte chunks in LDS so
+//    fragment reads of 16 rows 256 B apart hit distinct banks.
 //  * A job dequantises both operands exactly to fp16 in registers and issues
-//    v_mfma_f32_16x16x32_f16: two 16-row weight fragments x one or two
-//    16-token fragments, 8 steps per unit.  K is permuted identically on both
-//    sides (lane group q of a unit holds elements [64q, 64q+64)).
-//  * After the last unit of an item-chunk the wave scales by ga * gb[e] and
-//    stores its 32 x ntok outputs.
+//    v_mfma_f32_16x16x32_f16: four 16-row weight fragments x one or two
+//    16-token fragments, 16 steps per job (K is permuted identically on both
+//    sides).  Each token fragment is dequantised once per step and reused by
+//    the four weight fragments.
+//  * After the last slice of an item-chunk the wave scales by ga * gb[e] and
+//    stores its 64 x ntok outputs.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -35,16 +43,31 @@ namespace {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-constexpr int kWaves = 8;
+#ifndef NVFP4_GROUPED_FRAGS
+#define NVFP4_GROUPED_FRAGS 4
+#endif
+#ifndef NVFP4_GROUPED_WAVES
+#define NVFP4_GROUPED_WAVES 4
+#endif
+constexpr int kWaves = NVFP4_GROUPED_WAVES;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32;                        // weight rows per item
-constexpr int kUnitK = 256;                      // K elements per job
-constexpr int kSlots = 3;                        // LDS ring depth per wave
-constexpr int kSlotNib = kRows * (kUnitK / 2);   // 4096 B of nibbles
-constexpr int kSlotBytes = kSlotNib + kRows * (kUnitK / 16);  // + 512 B of scales
+constexpr int kFrags = NVFP4_GROUPED_FRAGS;      // 16-row weight fragments per item
+constexpr int kRows = 16 * kFrags;               // weight rows per item
+constexpr int kJobK = 512;                       // K elements per job
+#ifndef NVFP4_GROUPED_SLOTS
+#define NVFP4_GROUPED_SLOTS 2
+#endif
+constexpr int kSlots = NVFP4_GROUPED_SLOTS;      // LDS ring depth per wave
+constexpr int kRowNib = kJobK / 2;               // 256 B of nibbles per row per job
+constexpr int kRowSc = kJobK / 16;               // 32 B of scales per row per job
+constexpr int kSlotNib = kRows * kRowNib;        // nibbles of one job
+constexpr int kSlotBytes = kSlotNib + kRows * kRowSc;  // + its scales
 constexpr int kWaveLds = kSlots * kSlotBytes;
-constexpr int kLoadsPerJob = 12;                 // memory instructions per job
-constexpr uint32_t kOob = 0xFFFFFFF0u;           // offset past every operand
+constexpr int kNibLoads = kRows / 4;             // 16-byte DMAs of nibbles (4 rows each)
+constexpr int kScLoads = kRows / 32;             // 16-byte DMAs of scales (32 rows each)
+constexpr int kLoadsPerJob = kNibLoads + kScLoads + 10;  // memory instructions per job
+static_assert(kFrags % 2 == 0, "scale DMAs cover 32 rows");
+constexpr uint32_t kOob = 0xFFFFFFF0u;           // offset past every operand (reads zero)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -53,14 +76,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 __device__ __forceinline__ void dma16(const void* p, uint32_t bytes, uint32_t voff, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(p, bytes), (lds_void_ptr)lds, 16, voff, 0, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void* p, uint32_t bytes, uint32_t voff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(p, bytes), (lds_void_ptr)lds, 4, voff, 0, 0, 0);
-}
 __device__ __forceinline__ u32x4 ld16(const void* p, uint32_t bytes, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(p, bytes), voff, 0, 0));
 }
-__device__ __forceinline__ uint32_t ld4(const void* p, uint32_t bytes, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(rsrc(p, bytes), voff, 0, 0);
+__device__ __forceinline__ u32x2 ld8(const void* p, uint32_t bytes, uint32_t voff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc(p, bytes), voff, 0, 0));
 }
 
 template <int N>
@@ -75,7 +95,7 @@ struct Cursor {
   int e, n0;             // expert and first weight row of the item
   int r0, r1;            // the expert's token rows [r0, r1)
   int c0;                // first token row of the current chunk
-  int u;                 // current K unit
+  int u;                 // current K slice (job) of kJobK elements
 };
 
 struct Shape {
@@ -122,12 +142,14 @@ __device__ __forceinline__ void advance(const Shape& sh, const int32_t* __restri
   seek_item(sh, m_offsets, c.item + sh.stride, c);
 }
 
+__device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
+
 struct XFrags {
-  u32x4 q0[2], q1[2];  // token fragments 0, 1: 32 nibble bytes each
-  uint32_t s[2];       // their 4 scale bytes
+  u32x4 q[2][4];  // token fragments 0, 1: 64 nibble bytes each
+  u32x2 s[2];     // their 8 scale bytes
 };
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_grouped_kernel(
+__global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
     Shape sh, const int32_t* __restrict__ m_offsets, int K, const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
     const float* __restrict__ a_g, const uint8_t* __restrict__ b_q,
     const uint8_t* __restrict__ b_s, const float* __restrict__ b_g, void* __restrict__ y,
@@ -143,100 +165,126 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_grouped_kernel(
   const uint32_t xq_bytes = (uint32_t)sh.total_m * qrow, xs_bytes = (uint32_t)sh.total_m * srow;
   const float ga = a_g[0];
 
-  // per-lane parts of the weight load offsets (row within the item, byte
-  // within the unit); direct load k of 16 B covers rows 8k .. 8k+7
-  const uint32_t wrow16 = (uint32_t)(lane >> 3), wchunk = (uint32_t)(lane & 7) * 16;
-  const uint32_t wrow4 = (uint32_t)(lane >> 2), wpart = (uint32_t)(lane & 3) * 4;
+  // Load offsets = a per-lane constant + a scalar per job.  Weight nibble
+  // load k (16 B per lane) covers item rows 4k .. 4k+3: lane L takes row
+  // 4k + L/16 and physical 16-byte chunk L%16 of its 256-byte LDS row, which
+  // holds logical chunk (L%16) ^ (row%16).  The scale load covers all 32 rows
+  // (lane L: row L/2, half L%2).  Token fragment g holds chunk rows 16g+li.
+  // Offsets stay in the range-checked vector operand, so weight rows past N
+  // read as zero; token rows outside the expert's chunk get an out-of-range
+  // offset (zero, and no memory traffic).
+  uint32_t wq_lane[kNibLoads], xq_lane[2], xs_lane[2];
+#pragma unroll
+  for (int k = 0; k < kNibLoads; ++k) {
+    const uint32_t row = 4u * k + (uint32_t)(lane >> 4);
+    wq_lane[k] = row * qrow + (((uint32_t)(lane & 15) ^ (row & 15u)) << 4);
+  }
+  const uint32_t ws_lane = (uint32_t)(lane >> 1) * srow + (uint32_t)(lane & 1) * 16u;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    xq_lane[g] = (16u * g + (uint32_t)li) * qrow + (uint32_t)lq * 64u;
+    xs_lane[g] = (16u * g + (uint32_t)li) * srow + (uint32_t)lq * 8u;
+  }
 
   XFrags xs[kSlots];
 
   // Loads of the job at `c` into slot S: weights to LDS, activations to
-  // registers.  Always kLoadsPerJob memory instructions.
+  // registers.  Always kLoadsPerJob memory instructions; a finished wave
+  // pads with loads of expert 0's first slice.
   auto issue = [&](const Cursor& c, auto sc) {
     constexpr int S = decltype(sc)::value;
     const bool live = c.item < sh.n_items;
     const int e = live ? c.e : 0;
     const uint8_t* wq = b_q + (int64_t)e * sh.N * qrow;
     const uint8_t* ws = b_s + (int64_t)e * sh.N * srow;
+    const uint32_t wq_job = live ? (uint32_t)c.n0 * qrow + (uint32_t)c.u * kRowNib : 0u;
+    const uint32_t ws_job = live ? (uint32_t)c.n0 * srow + (uint32_t)c.u * kRowSc : 0u;
+    const uint32_t xq_job = (uint32_t)c.c0 * qrow + (uint32_t)c.u * kRowNib;
+    const uint32_t xs_job = (uint32_t)c.c0 * srow + (uint32_t)c.u * kRowSc;
     uint8_t* slot = ring + S * kSlotBytes;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t row = (uint32_t)(c.n0) + 8u * k + wrow16;
-      dma16(wq, wq_bytes, live ? row * qrow + (uint32_t)c.u * 128u + wchunk : kOob,
-            slot + k * 1024);
-    }
+    for (int k = 0; k < kNibLoads; ++k) dma16(wq, wq_bytes, wq_job + wq_lane[k], slot + k * 1024);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t row = (uint32_t)(c.n0) + 16u * k + wrow4;
-      dma4(ws, ws_bytes, live ? row * srow + (uint32_t)c.u * 16u + wpart : kOob,
-           slot + kSlotNib + k * 256);
-    }
+    for (int m = 0; m < kScLoads; ++m)
+      dma16(ws, ws_bytes, ws_job + 32u * m * srow + ws_lane, slot + kSlotNib + m * 1024);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int t = c.c0 + 16 * g + li;
-      const bool ok = live && t < c.r1;
-      const uint32_t qo = ok ? (uint32_t)t * qrow + (uint32_t)c.u * 128u + (uint32_t)lq * 32u : kOob;
-      const uint32_t so = ok ? (uint32_t)t * srow + (uint32_t)c.u * 16u + (uint32_t)lq * 4u : kOob;
-      xs[S].q0[g] = ld16(a_q, xq_bytes, qo);
-      xs[S].q1[g] = ld16(a_q, xq_bytes, ok ? qo + 16u : kOob);
-      xs[S].s[g] = ld4(a_s, xs_bytes, so);
+      // token rows outside the expert's chunk are not fetched at all
+      const bool ok = live && c.c0 + 16 * g + li < c.r1;
+      const uint32_t qo = ok ? xq_job + xq_lane[g] : kOob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[S].q[g][i] = ld16(a_q, xq_bytes, ok ? qo + 16u * i : kOob);
+      xs[S].s[g] = ld8(a_s, xs_bytes, ok ? xs_job + xs_lane[g] : kOob);
     }
   };
 
-  f32x4 acc[2][2];
+  f32x4 acc[kFrags][2];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < kFrags; ++f)
 #pragma unroll
     for (int g = 0; g < 2; ++g) acc[f][g] = f32x4{0, 0, 0, 0};
 
   // One job from slot S (its loads have landed), then the item-chunk
-  // epilogue if this was its last unit.
+  // epilogue if this was its last slice.
   auto compute = [&](const Cursor& c, auto sc) {
     constexpr int S = decltype(sc)::value;
     const uint8_t* slot = ring + S * kSlotBytes;
-    u32x4 wlo[2], whi[2];
-    Scales sw[2];
+    u32x4 w[kFrags][4];
+    Scales sw[kFrags][2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < kFrags; ++f) {
       const int row = 16 * f + li;
-      wlo[f] = *reinterpret_cast<const u32x4*>(slot + row * 128 + lq * 32);
-      whi[f] = *reinterpret_cast<const u32x4*>(slot + row * 128 + lq * 32 + 16);
-      sw[f] = to_scales(*reinterpret_cast<const uint32_t*>(slot + kSlotNib + row * 16 + lq * 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[f][i] = *reinterpret_cast<const u32x4*>(slot + row * kRowNib + (((4 * lq + i) ^ (row & 15)) << 4));
+      const u32x2 s8 = *reinterpret_cast<const u32x2*>(slot + kSlotNib + row * kRowSc + lq * 8);
+      sw[f][0] = to_scales(s8[0]);
+      sw[f][1] = to_scales(s8[1]);
     }
-    const Scales sx0 = to_scales(xs[S].s[0]);
+    const Scales sx0[2] = {to_scales(xs[S].s[0][0]), to_scales(xs[S].s[0][1])};
     const int ntok = min(32, c.r1 - c.c0);
+    // step T (0..15) uses dword T of the lane's 64 bytes: block T/2, i.e.
+    // scale pair word T/8, block (T/2) % 4 within it
     if (ntok > 16) {  // wave-uniform
-      const Scales sx1 = to_scales(xs[S].s[1]);
-      static_for<8>([&](auto tc) {
-        constexpr int T = decltype(tc)::value;
-        const uint32_t w0 = T < 4 ? wlo[0][T & 3] : whi[0][T & 3];
-        const uint32_t w1 = T < 4 ? wlo[1][T & 3] : whi[1][T & 3];
-        const uint32_t x0 = T < 4 ? xs[S].q0[0][T & 3] : xs[S].q1[0][T & 3];
-        const uint32_t x1 = T < 4 ? xs[S].q0[1][T & 3] : xs[S].q1[1][T & 3];
-        const f16x8 a0 = dequant_step<T>(w0, sw[0]), a1 = dequant_step<T>(w1, sw[1]);
-        const f16x8 b0 = dequant_step<T>(x0, sx0), b1 = dequant_step<T>(x1, sx1);
-        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[0][0], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b0, acc[1][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[1][1], 0, 0, 0);
+      // fresh copies of the shared operands, so the compiler cannot hoist
+      // the two branches' common dequantisation above the branch (that
+      // would keep all of it live at once)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) opaque(w[f][i]);
+        opaque(xs[S].q[0][i]);
+      }
+      const Scales sx1[2] = {to_scales(xs[S].s[1][0]), to_scales(xs[S].s[1][1])};
+      static_for<16>([&](auto tc) {
+        constexpr int T = decltype(tc)::value, Q = T / 4, D = T % 4, H = T / 8, TT = T % 8;
+        const f16x8 b0 = dequant_step<TT>(xs[S].q[0][Q][D], sx0[H]);
+        const f16x8 b1 = dequant_step<TT>(xs[S].q[1][Q][D], sx1[H]);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) {
+          const f16x8 a = dequant_step<TT>(w[f][Q][D], sw[f][H]);
+          acc[f][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, acc[f][0], 0, 0, 0);
+          acc[f][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b1, acc[f][1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep each step's dequant beside its MFMAs
       });
     } else {
-      static_for<8>([&](auto tc) {
-        constexpr int T = decltype(tc)::value;
-        const uint32_t w0 = T < 4 ? wlo[0][T & 3] : whi[0][T & 3];
-        const uint32_t w1 = T < 4 ? wlo[1][T & 3] : whi[1][T & 3];
-        const uint32_t x0 = T < 4 ? xs[S].q0[0][T & 3] : xs[S].q1[0][T & 3];
-        const f16x8 a0 = dequant_step<T>(w0, sw[0]), a1 = dequant_step<T>(w1, sw[1]);
-        const f16x8 b0 = dequant_step<T>(x0, sx0);
-        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[0][0], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b0, acc[1][0], 0, 0, 0);
+      static_for<16>([&](auto tc) {
+        constexpr int T = decltype(tc)::value, Q = T / 4, D = T % 4, H = T / 8, TT = T % 8;
+        const f16x8 b0 = dequant_step<TT>(xs[S].q[0][Q][D], sx0[H]);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) {
+          const f16x8 a = dequant_step<TT>(w[f][Q][D], sw[f][H]);
+          acc[f][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, acc[f][0], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       });
     }
     if (c.u == sh.nunits - 1) {
       // acc[f][g] reg r: weight row n0 + 16f + 4*lq + r, token c0 + 16g + li
       const float alpha = ga * b_g[c.e];
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < kFrags; ++f)
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const int tok = 16 * g + li;
@@ -255,30 +303,24 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_grouped_kernel(
   Cursor lc, cc;
   seek_item(shl, m_offsets, blockIdx.x * kWaves + wave, lc);
   cc = lc;
-  issue(lc, std::integral_constant<int, 0>{});
-  advance(shl, m_offsets, lc);
-  issue(lc, std::integral_constant<int, 1>{});
-  advance(shl, m_offsets, lc);
-  // jobs rotate through slots 0, 1, 2; the loads of job j+2 go out before
-  // job j waits for its own (two younger jobs may stay in flight)
-  while (cc.item < shl.n_items) {
-    issue(lc, std::integral_constant<int, 2>{});
+  static_for<kSlots - 1>([&](auto sc) {
+    issue(lc, sc);
     advance(shl, m_offsets, lc);
-    wait_vmcnt<2 * kLoadsPerJob>();
-    compute(cc, std::integral_constant<int, 0>{});
-    advance(shl, m_offsets, cc);
-    if (cc.item >= shl.n_items) break;
-    issue(lc, std::integral_constant<int, 0>{});
-    advance(shl, m_offsets, lc);
-    wait_vmcnt<2 * kLoadsPerJob>();
-    compute(cc, std::integral_constant<int, 1>{});
-    advance(shl, m_offsets, cc);
-    if (cc.item >= shl.n_items) break;
-    issue(lc, std::integral_constant<int, 1>{});
-    advance(shl, m_offsets, lc);
-    wait_vmcnt<2 * kLoadsPerJob>();
-    compute(cc, std::integral_constant<int, 2>{});
-    advance(shl, m_offsets, cc);
+  });
+  // jobs rotate through the slots; the loads of job j + kSlots - 1 go out
+  // before job j waits for its own (the younger jobs may stay in flight)
+  bool more = cc.item < shl.n_items;
+  while (more) {
+    static_for<kSlots>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      if (!more) return;
+      issue(lc, std::integral_constant<int, (S + kSlots - 1) % kSlots>{});
+      advance(shl, m_offsets, lc);
+      wait_vmcnt<(kSlots - 1) * kLoadsPerJob>();
+      compute(cc, sc);
+      advance(shl, m_offsets, cc);
+      more = cc.item < shl.n_items;
+    });
   }
   wait_vmcnt<0>();  // padding loads land before the wave exits
 }
@@ -305,7 +347,7 @@ hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, int64_t tota
   if (attr != hipSuccess) return attr;
   int64_t grid = ((n_items + kWaves - 1) / kWaves);
   if (grid > num_cu) grid = num_cu;  // persistent: one workgroup per CU
-  Shape sh{(int)N, (int)(K / kUnitK), (int)tiles, (int)n_items, (int)grid * kWaves, total_m};
+  Shape sh{(int)N, (int)(K / kJobK), (int)tiles, (int)n_items, (int)grid * kWaves, total_m};
   gemm_grouped_kernel<<<(unsigned)grid, kThreads, smem, stream>>>(sh, m_offsets, (int)K, a.q, a.s, a.g, b.q,
                                                                   b.s, b.g, y, y_dtype, ld_y);
   return hipGetLastError();

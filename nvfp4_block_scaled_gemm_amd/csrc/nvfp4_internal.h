@@ -40,7 +40,7 @@ hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a,
                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                               hipStream_t stream);
 
-// gemm_grouped.hip: K % 256 == 0, operands < 4 GiB.
+// gemm_grouped.hip: K % 512 == 0, operands < 4 GiB.
 hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, int64_t total_m,
                                int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                                void* y, int y_dtype, int64_t ld_y, hipStream_t stream);

@@ -44,7 +44,8 @@ def _run(counts, N, K, out, seed):
     ([0, 0, 7], 64, 512),
     ([17], 48, 2048),
     ([1] * 20, 40, 256),
-    ([33, 64, 2, 0, 31, 32, 130], 200, 768),
+    ([33, 64, 2, 0, 31, 32, 130], 200, 1536),
+    ([33, 0, 2, 31, 16], 72, 768),
     ([5, 9], 30, 48),
 ])
 def test_ragged_groups(counts, N, K):
@@ -53,7 +54,7 @@ def test_ragged_groups(counts, N, K):
 
 
 def test_all_groups_empty_but_last():
-    _run([0] * 15 + [4], 64, 256, "f32", seed=3)
+    _run([0] * 15 + [4], 64, 512, "f32", seed=3)
 
 
 def _moe_case(proj: str):
