@@ -5,7 +5,7 @@ import torch
 
 import nvfp4_block_scaled_gemm_amd as nv
 import workloads as wl
-from oracle import check_gemm, gemm_ref, grouped_gemm_ref
+from oracle import check_gemm, gemm_ref, grouped_gemm_ref, pack_nibbles
 from tests.gpu_util import (assert_bytes_equal, need_gpu, note, np_, oracle_global_scale,
                             oracle_quantize)
 
@@ -51,6 +51,48 @@ def _run(counts, N, K, out, seed):
 def test_ragged_groups(counts, N, K):
     for out in ("f32", "bf16"):
         _run(counts, N, K, out, seed=sum(counts) + N + K)
+
+
+@pytest.mark.parametrize("counts", [[512], [0, 512, 512], [5], [20, 0, 17, 3]])
+def test_exhaustive_dequant_identity(counts):
+    """Each group's A rows are one-hot rows (nibble 1.0, scale 1.0, g = 1) and
+    each expert's W [8, 512] holds every nibble under every finite scale byte,
+    so each group's y is exactly columns of W_e_dq, read back bit for bit.
+    A group of 512 rows reads every column of its expert (all 4096
+    nibble/scale pairs); the small groups run chunks with one and with two
+    16-token fragments.  K = 512 runs the streaming grouped kernel."""
+    need_gpu()
+    K, N = 512, 8
+    G = len(counts)
+    off = wl.ragged_offsets(counts)
+    total = int(off[-1])
+    nib = np.zeros((total, K), dtype=np.uint8)
+    for e in range(G):
+        for i in range(int(off[e]), int(off[e + 1])):
+            nib[i, 37 * (i - int(off[e])) % K] = 0x2   # 37 is odd: distinct columns
+    aq = pack_nibbles(nib)
+    as_ = np.full((total, K // 16), 0x38, np.uint8)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[0x7F], codes[0xFF] = 0x3F, 0xBF                 # NaN codes replaced
+    rng = np.random.default_rng(1)
+    bq = np.zeros((G, N, K // 2), dtype=np.uint8)
+    bs = np.zeros((G, N, K // 16), dtype=np.uint8)
+    for e in range(G):
+        wn = np.zeros((N, K), dtype=np.uint8)
+        for blk in range(N * K // 16):
+            r, c = divmod(blk, K // 16)
+            wn[r, 16 * c:16 * c + 16] = rng.permutation(16)
+        bq[e] = pack_nibbles(wn)
+        bs[e] = np.roll(codes, 64 * e).reshape(N, K // 16)
+    bg = np.ones(G, dtype=np.float32)
+    dev = "cuda"
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)  # noqa: E731
+    note(f"grouped exhaustive dequant counts={counts}")
+    y = nv.nvfp4_grouped_gemm(off.to(dev), total, (t(aq), t(as_), torch.ones(1, device=dev)),
+                              (t(bq), t(bs), t(bg)), out_dtype="f32")
+    torch.cuda.synchronize()
+    y_ref, _ = grouped_gemm_ref(off.numpy(), aq, as_, np.float32(1), bq, bs, bg)
+    assert np.array_equal(np_(y), y_ref.astype(np.float32))
 
 
 def test_all_groups_empty_but_last():
