@@ -82,18 +82,15 @@ __device__ __forceinline__ void chunk_partial(const Rows& w, const Rows& x, int 
     for (int g = 0; g < 2; ++g) acc[f][g] = f32x4{0, 0, 0, 0};
   for (int ub = wave; ub < nunits; ub += kWaves * kMaxUnits) {
     Unit w0[kMaxUnits], w1[kMaxUnits], x0[kMaxUnits], x1[kMaxUnits];
-    // every load of the round first: weights, then activations
+    // every load of the round first, unit by unit (weights, then that
+    // unit's activations), so unit i's products wait only for loads issued
+    // up to unit i and overlap the later units' transfers
 #pragma unroll
     for (int i = 0; i < kMaxUnits; ++i) {
       const int u = ub + i * kWaves;
       const bool in = u < nunits;
       w0[i] = load_unit(w.q0, w.s0, u, lq, in && w.v0);
       w1[i] = load_unit(w.q1, w.s1, u, lq, in && w.v1);
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxUnits; ++i) {
-      const int u = ub + i * kWaves;
-      const bool in = u < nunits;
       x0[i] = load_unit(x.q0, x.s0, u, lq, in && x.v0);
       if constexpr (NX == 2) x1[i] = load_unit(x.q1, x.s1, u, lq, in && x.v1);
     }

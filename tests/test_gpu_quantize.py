@@ -71,6 +71,61 @@ def test_special_values():
     _check(x.to(torch.bfloat16))
 
 
+def _e4m3_values():
+    """The 127 finite non-negative E4M3 values, by code (bit fields)."""
+    out = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        out.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("gmul", [1.0, 1.5, 0.375])
+def test_scale_code_tie_sweep(gmul):
+    """Block maxima exactly on every E4M3 midpoint (times 6g), and one fp32
+    step either side, with g = gmul exactly (first block holds 2688 * gmul)."""
+    v = _e4m3_values()
+    mids = (v[:-1] + v[1:]) / 2 * 6 * gmul
+    vals = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                           np.nextafter(mids.astype(np.float32), np.float32(0))]).astype(np.float32)
+    x = np.zeros((len(vals) + 1, 16), dtype=np.float32)
+    x[0, 0] = 2688.0 * gmul
+    x[1:, 5] = vals
+    x[1:, 9] = -vals / 3                     # a second, smaller element per block
+    _check(torch.from_numpy(x))
+
+
+@pytest.mark.parametrize("gmul", [1.0, 1.5])
+def test_element_threshold_sweep(gmul):
+    """For every non-zero scale code, elements exactly on each E2M1 midpoint
+    times the block scale, and one fp32 step either side (g = gmul)."""
+    v = _e4m3_values()
+    mid2 = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    rows = [np.zeros(16, np.float32)]
+    rows[0][0] = 2688.0 * gmul
+    for c in range(1, 127):
+        S = v[c] * gmul
+        for side in (0, 1, 2):
+            blk = np.zeros(16, np.float32)
+            blk[0] = np.float32(6 * S)            # block max 6 S -> scale code c exactly
+            t = (mid2 * S).astype(np.float32)
+            if side == 1:
+                t = np.nextafter(t, np.float32(np.inf))
+            elif side == 2:
+                t = np.nextafter(t, np.float32(0))
+            blk[1:8] = t
+            blk[8:15] = -t
+            rows.append(blk)
+    _check(torch.from_numpy(np.stack(rows)))
+
+
+@pytest.mark.parametrize("scale", [1e-30, 1e-41, 3e-45])
+def test_tiny_magnitudes(scale):
+    """Global scales far below the normal range (fp32 subnormal inputs too)."""
+    x = (wl.randn((16, 256), 31, "fp32") * scale).to(torch.float32)
+    _check(x)
+
+
 def test_static_global_scale_path():
     x = wl.randn((33, 512), 9, "bf16", True)
     _check(x, global_scale=0.001953125)               # saturates the outliers
