@@ -16,7 +16,8 @@ Prints one JSON line.  ``value`` is 2*M*N*K flop per step / step time
 over its average launch time (HIP events on the launch stream) against the
 fp16 dense matrix-core peak, since that is the MFMA family the kernel
 issues.  ``decode`` holds the skinny M = 1, 16, 32 GEMMs over 16 rotating copies of W
-(604 MB, so the 256 MB Infinity Cache cannot hold them) and ``moe_grouped``
+(604 MB, so the 256 MB Infinity Cache cannot hold them), timed as 128
+back-to-back launches between one pair of events, and ``moe_grouped``
 the two grouped expert GEMMs, each against HBM peak.
 ``cpu_baseline`` times the CPU oracle on a bounded row slice of the same step.
 """
@@ -175,13 +176,26 @@ def main():
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in evs) / reps
 
+    def timed_batch(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
     decode = {}
     for m in (1, 16, 32):
         dcfg = wl.DECODE[m]
         xd = nv.nvfp4_quantize(wl.randn((m, dcfg.K), wl.seed_for(2, 0), "bf16").to(dev))
         yd = torch.empty((m, dcfg.N), dtype=torch.bfloat16, device=dev)
-        timed(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 16)
-        ms = timed(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 128)
+        # back-to-back launches between one pair of events (a decode step
+        # issues its GEMMs back to back); per-launch events would add their
+        # own overhead to a ~10 us kernel
+        timed_batch(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 16)
+        ms = timed_batch(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 128)
         nbytes = dcfg.N * dcfg.K * 9 // 16 + m * dcfg.K * 9 // 16 + m * dcfg.N * 2
         gbs = nbytes / (ms * 1e-3) / 1e9
         decode[f"m{m}"] = {"us": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
