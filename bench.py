@@ -18,7 +18,8 @@ fp16 dense matrix-core peak, since that is the MFMA family the kernel
 issues.  ``decode`` holds the skinny M = 1, 16, 32 GEMMs over 16 rotating copies of W
 (604 MB, so the 256 MB Infinity Cache cannot hold them), timed as 128
 back-to-back launches between one pair of events, and ``moe_grouped``
-the two grouped expert GEMMs, each against HBM peak.
+the two grouped expert GEMMs, each against HBM peak; ``large`` the
+M = N = K = 16384 outlier workload (quantiser on x alone, then the GEMM).
 ``cpu_baseline`` times the CPU oracle on a bounded row slice of the same step.
 """
 from __future__ import annotations
@@ -238,6 +239,31 @@ def main():
                      "tflops": round(2.0 * total * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
         del bq, bs, bg, a, ym
 
+    # Large outlier workload M = N = K = 16384 (1 % of entries x50): the
+    # quantiser on x timed alone (two reads of x + the packed writes), then
+    # the GEMM.  Inputs are drawn on the GPU (same recipe, CUDA generator).
+    lcfg = wl.LARGE
+    xl = wl.randn((lcfg.M, lcfg.K), wl.seed_for(4, 0), "bf16", True, device=dev)
+    wlq = nv.nvfp4_quantize(wl.randn((lcfg.N, lcfg.K), wl.seed_for(4, 1), "bf16", True, device=dev))
+    xlq = nv.nvfp4_quantize(xl)
+    wsl = torch.empty(max(nv.nvfp4_quantize_workspace_bytes(lcfg.M, lcfg.K), 4), dtype=torch.uint8,
+                      device=dev)
+    timed_batch(lambda i: nv.nvfp4_quantize(xl, out=xlq, workspace=wsl), 3)
+    q_ms = timed_batch(lambda i: nv.nvfp4_quantize(xl, out=xlq, workspace=wsl), 20)
+    q_bytes = 2 * lcfg.M * lcfg.K * 2 + lcfg.M * lcfg.K * 9 // 16
+    yl = torch.empty((lcfg.M, lcfg.N), dtype=torch.bfloat16, device=dev)
+    timed_batch(lambda i: nv.nvfp4_gemm(xlq, wlq, "bf16", y=yl), 1)
+    lg_ms = timed_batch(lambda i: nv.nvfp4_gemm(xlq, wlq, "bf16", y=yl), 5)
+    lflop = 2.0 * lcfg.M * lcfg.N * lcfg.K
+    large = {"workload": lcfg.name,
+             "quantize_x_us": round(q_ms * 1e3, 2), "quantize_bytes": q_bytes,
+             "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+             "quantize_frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             "gemm_us": round(lg_ms * 1e3, 1),
+             "gemm_tflops": round(lflop / (lg_ms * 1e-3) / 1e12, 2),
+             "gemm_frac_mfma": round(lflop / (lg_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4)}
+    del xl, wlq, xlq, yl
+
     out = {
         "metric": "NVFP4 GEMM TFLOPS + % of MFMA/HBM roofline (M=4096,N=K=8192; M=16 decode)",
         "value": round(value, 2),
@@ -263,6 +289,7 @@ def main():
         "decode": dict(decode, workload="decode_m{1,16,32}_n8192_k8192", peak_GBps=PEAK_HBM_GBS,
                        weights="16 rotating copies (cache-cold)"),
         "moe_grouped": dict(moe, peak_GBps=PEAK_HBM_GBS),
+        "large": large,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, args.cpu_rows)
