@@ -102,8 +102,11 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of x in the CPU oracle sample (4096 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
-                    help="copy: a plain 1 GiB device copy, for HBM counter calibration")
+    ap.add_argument("--mode", choices=["bench", "copy", "sweep"], default="bench",
+                    help="copy: a plain 1 GiB device copy, for HBM counter calibration; "
+                         "sweep: the GEMM at growing tile counts (1 .. 1024 workgroups), "
+                         "to see how throughput per CU and the clock change with the "
+                         "number of busy CUs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -123,6 +126,29 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read_per_copy": src.numel() * 4,
                           "bytes_written_per_copy": src.numel() * 4, "copies": args.steps}))
+        return
+
+    if args.mode == "sweep":
+        for (M, N, K) in ((256, 256, 8192), (1024, 1024, 8192), (2048, 4096, 8192),
+                          (4096, 4096, 8192), (4096, 8192, 8192), (8192, 8192, 8192)):
+            a = nv.nvfp4_quantize(wl.randn((M, K), 1, "bf16", device=dev))
+            b = nv.nvfp4_quantize(wl.randn((N, K), 2, "bf16", device=dev))
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                nv.nvfp4_gemm(a, b, "bf16", y=y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                nv.nvfp4_gemm(a, b, "bf16", y=y)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            tiles = -(-M // 256) * -(-N // 256)
+            print(json.dumps({"mode": "sweep", "M": M, "N": N, "K": K, "workgroups": tiles,
+                              "us": round(us, 2), "tflops": round(2 * M * N * K / us / 1e6, 1),
+                              "tflops_per_busy_cu": round(2 * M * N * K / us / 1e6 / min(tiles, 256), 3)}),
+                  flush=True)
         return
 
     cfg = wl.LINEAR
