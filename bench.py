@@ -18,7 +18,8 @@ fp16 dense matrix-core peak, since that is the MFMA family the kernel
 issues.  ``decode`` holds the skinny M = 1, 16, 32 GEMMs over 16 rotating copies of W
 (604 MB, so the 256 MB Infinity Cache cannot hold them), timed as 128
 back-to-back launches between one pair of events, and ``moe_grouped``
-the two grouped expert GEMMs, each against HBM peak; ``large`` the
+the two grouped expert GEMMs, each against HBM peak; ``mid_m`` GEMMs with
+M = 64 .. 1024 on the same rotating weights; ``large`` the
 M = N = K = 16384 outlier workload (quantiser on x alone, then the GEMM).
 ``cpu_baseline`` times the CPU oracle on a bounded row slice of the same step.
 """
@@ -228,6 +229,16 @@ def main():
         decode[f"m{m}"] = {"us": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
                            "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                            "tflops": round(2.0 * m * dcfg.N * dcfg.K / (ms * 1e-3) / 1e12, 3)}
+    # mid-range M (the pages' weak region between decode and large batches),
+    # same rotating weights
+    mid_m = {}
+    for m in (64, 128, 256, 512, 1024):
+        xm = nv.nvfp4_quantize(wl.randn((m, cfg.K), wl.seed_for(2, 1), "bf16").to(dev))
+        ym = torch.empty((m, cfg.N), dtype=torch.bfloat16, device=dev)
+        timed_batch(lambda i: nv.nvfp4_gemm(xm, copies[i % 16], "bf16", y=ym), 8)
+        ms = timed_batch(lambda i: nv.nvfp4_gemm(xm, copies[i % 16], "bf16", y=ym), 32)
+        mid_m[f"m{m}"] = {"us": round(ms * 1e3, 2),
+                          "tflops": round(2.0 * m * cfg.N * cfg.K / (ms * 1e-3) / 1e12, 1)}
     del copies
 
     # MoE grouped GEMMs: 512 tokens, top-8 of 256 experts (seeded softmax
@@ -316,6 +327,7 @@ def main():
                        weights="16 rotating copies (cache-cold)"),
         "moe_grouped": dict(moe, peak_GBps=PEAK_HBM_GBS),
         "large": large,
+        "mid_m": dict(mid_m, workload="m{64..1024}_n8192_k8192, 16 rotating weight copies"),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, args.cpu_rows)

@@ -102,7 +102,7 @@ int nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t col
  * a_q [M, K/2], a_s [M, K/16], b_q [N, K/2], b_s [N, K/16] are dense.
  * y [M, N] has row stride ld_y >= N elements of y_dtype.
  * Any M, N >= 0; K % 16 == 0.  Shapes are dispatched to a decode kernel
- * (M <= 32), an MFMA tile kernel, or a general kernel for unaligned K.
+ * (M <= 128), an MFMA tile kernel, or a general kernel for unaligned K.
  */
 int nvfp4_gemm(int64_t M, int64_t N, int64_t K,
                const uint8_t* a_q, const uint8_t* a_s, const float* a_g,

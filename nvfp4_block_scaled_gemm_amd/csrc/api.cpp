@@ -89,7 +89,7 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_
   hipStream_t st = (hipStream_t)stream;
   const int dt = (int)y_dtype;
   // K == 0: the sum is empty; the general kernel writes zeros.
-  if (K > 0 && M <= 32 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256) &&
+  if (K > 0 && M <= 128 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256) &&
       offsets32_ok(N, K))
     return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st));
   if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128) &&

@@ -399,8 +399,15 @@ hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOp
 
 hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                             void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
-  if (M >= 256 && N >= 256)
+  // The largest tile that still fills the chip for at least one round (the
+  // larger the tile, the fewer dequantisations per MFMA): 256 x 256, then
+  // 256 x 128, else 128 x 128 (4x the workgroups of 256 x 256; two fit per
+  // CU).
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (M >= 256 && N >= 256 && tiles(256, 256) >= 256)
     return launch_cfg<256, 256, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream);
+  if (M >= 256 && N >= 128 && tiles(256, 128) >= 256)
+    return launch_cfg<256, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream);
   return launch_cfg<128, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream);
 }
 

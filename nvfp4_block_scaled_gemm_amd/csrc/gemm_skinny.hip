@@ -1,4 +1,5 @@
-// Weight-streaming NVFP4 GEMM for few rows of x: the decode case (M <= 32).
+// Weight-streaming NVFP4 GEMM for few rows of x: the decode case (up to 64
+// tokens per pass over the weights; the launcher runs up to two passes).
 //
 // The pages place these shapes far below the compute ridge: decode batches of
 // 16-64 tokens reach a small fraction of the big-GEMM rate (magik.net "The
@@ -19,7 +20,7 @@
 //    loads in flight and the products overlap the weight stream (loads
 //    under a branch would make it wait for all of them).
 //  * Products run on v_mfma_f32_16x16x32_f16 with weights as the 16-row A
-//    operand and up to 32 tokens as one or two B operands; both sides are
+//    operand and up to 64 tokens as one to four B operands; both sides are
 //    dequantised exactly to fp16 in registers.  K is permuted identically on
 //    both sides.
 //  * The 8 per-wave partial tiles are summed through LDS in a fixed order, so
@@ -34,7 +35,10 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWG = 32;   // weight rows (output columns) per workgroup
 constexpr int kUnitK = 256;      // K elements per wave step
-constexpr int kMaxUnits = 4;     // units per wave per round (K <= 8192 per round)
+// units per wave per round: 4 (K <= 8192 per round), 2 with four token
+// fragments (their registers)
+template <int NX>
+constexpr int max_units() { return NX > 2 ? 2 : 4; }
 constexpr uint32_t kOob = 0xFFFFFFF0u;  // offset past every operand (reads zero)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -70,18 +74,18 @@ struct Frag {
   bool ok;        // the row exists
 };
 
-// One token chunk (<= 16 * NX tokens) of the 32-row tile, over all of K;
-// leaves the wave's partial sums in acc[f][g] (weight fragment f, token
-// fragment g).
+// The tokens (<= 16 * NX) against the 32-row tile, over all of K; leaves the
+// wave's partial sums in acc[f][g] (weight fragment f, token fragment g).
 template <int NX>
 __device__ __forceinline__ void chunk_partial(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws,
                                               __amdgpu_buffer_rsrc_t xq, __amdgpu_buffer_rsrc_t xs,
-                                              const Frag (&w)[2], const Frag (&x)[2], int nunits,
-                                              int wave, f32x4 (&acc)[2][2]) {
+                                              const Frag (&w)[2], const Frag (&x)[4], int nunits,
+                                              int wave, f32x4 (&acc)[2][4]) {
+  constexpr int kMaxUnits = max_units<NX>();
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int g = 0; g < 2; ++g) acc[f][g] = f32x4{0, 0, 0, 0};
+    for (int g = 0; g < 4; ++g) acc[f][g] = f32x4{0, 0, 0, 0};
   for (int ub = wave; ub < nunits; ub += kWaves * kMaxUnits) {
     Unit wu[kMaxUnits][2], xu[kMaxUnits][NX];
 #pragma unroll
@@ -107,13 +111,11 @@ __device__ __forceinline__ void chunk_partial(__amdgpu_buffer_rsrc_t wq, __amdgp
         constexpr int T = decltype(tc)::value, Q = T / 4, D = T % 4;
         const f16x8 a0 = dequant_step<T>(wu[i][0].q[Q][D], sw[0]);
         const f16x8 a1 = dequant_step<T>(wu[i][1].q[Q][D], sw[1]);
-        const f16x8 b0 = dequant_step<T>(xu[i][0].q[Q][D], sx[0]);
-        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[0][0], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b0, acc[1][0], 0, 0, 0);
-        if constexpr (NX == 2) {
-          const f16x8 b1 = dequant_step<T>(xu[i][NX - 1].q[Q][D], sx[NX - 1]);
-          acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b1, acc[0][1], 0, 0, 0);
-          acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[1][1], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NX; ++g) {
+          const f16x8 b = dequant_step<T>(xu[i][g].q[Q][D], sx[g]);
+          acc[0][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, acc[0][g], 0, 0, 0);
+          acc[1][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b, acc[1][g], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep each step's dequant beside its MFMAs
       });
@@ -140,39 +142,48 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(
   const float alpha = a_g[0] * b_g[0];
 
   // weight rows of this lane: n0 + 16 f + li; token rows: 16 g + li
-  Frag w[2], x[2];
+  Frag w[2], x[4];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const uint32_t row = (uint32_t)(n0 + 16 * f + li);
     w[f] = Frag{row * qrow + (uint32_t)lq * 32u, row * srow + (uint32_t)lq * 4u, row < (uint32_t)N};
-    const uint32_t tok = (uint32_t)(16 * f + li);
-    x[f] = Frag{tok * qrow + (uint32_t)lq * 32u, tok * srow + (uint32_t)lq * 4u, tok < (uint32_t)M};
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t tok = (uint32_t)(16 * g + li);
+    x[g] = Frag{tok * qrow + (uint32_t)lq * 32u, tok * srow + (uint32_t)lq * 4u, tok < (uint32_t)M};
   }
 
-  f32x4 acc[2][2];
-  if (M > 16) chunk_partial<2>(wq, ws, xq, xs, w, x, nunits, wave, acc);  // uniform
+  f32x4 acc[2][4];
+  if (M > 32) chunk_partial<4>(wq, ws, xq, xs, w, x, nunits, wave, acc);  // uniform
+  else if (M > 16) chunk_partial<2>(wq, ws, xq, xs, w, x, nunits, wave, acc);
   else chunk_partial<1>(wq, ws, xq, xs, w, x, nunits, wave, acc);
 
-  // partial tiles -> LDS: acc[f][g] reg r is weight row 16f + 4*lq + r,
-  // token 16g + li
+  // Partial tiles -> LDS and a fixed-order sum over the waves, 32 tokens at
+  // a time: acc[f][g] reg r is weight row 16f + 4*lq + r, token 16g + li.
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int half = 0; half < 2; ++half) {
+    if (half * 32 >= M) break;  // uniform
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][16 * f + 4 * lq + r][16 * g + li] = acc[f][g][r];
-  __syncthreads();
-  // 1024 outputs (32 tokens x 32 weight rows), two per thread, summed over
-  // the waves in a fixed order
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
-  for (int h = 0; h < (32 * kRowsPerWG) / kThreads; ++h) {
-    const int o = tid + h * kThreads;
-    const int tok = o >> 5, wr = o & 31;
-    float s = 0.0f;
+        for (int r = 0; r < 4; ++r)
+          red[wave][16 * f + 4 * lq + r][16 * g + li] = acc[f][2 * half + g][r];
+    __syncthreads();
+    // 1024 outputs (32 tokens x 32 weight rows), two per thread
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) s += red[v][wr][tok];
-    const int n = n0 + wr;
-    if (tok < M && n < N) store_out(y, (int64_t)tok * ld_y + n, s * alpha, y_dtype);
+    for (int h = 0; h < (32 * kRowsPerWG) / kThreads; ++h) {
+      const int o = tid + h * kThreads;
+      const int tok = 32 * half + (o >> 5), wr = o & 31;
+      float s = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) s += red[v][wr][o >> 5];
+      const int n = n0 + wr;
+      if (tok < M && n < N) store_out(y, (int64_t)tok * ld_y + n, s * alpha, y_dtype);
+    }
+    __syncthreads();
   }
 }
 
@@ -181,9 +192,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(
 hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                               void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
   const int64_t tiles = (N + kRowsPerWG - 1) / kRowsPerWG;
-  gemm_decode_kernel<<<(unsigned)tiles, kThreads, 0, stream>>>(
-      (int)N, (int)K, (int)M, a.q, a.s, a.g, b.q, b.s, b.g, y, y_dtype, ld_y);
-  return hipGetLastError();
+  // up to 64 tokens per launch; more rows go in 64-row passes over W (the
+  // later passes find W in the Infinity Cache when it fits there)
+  const size_t ysize = y_dtype == 0 ? 4 : 2;
+  for (int64_t r0 = 0; r0 < M; r0 += 64) {
+    const int64_t m = M - r0 < 64 ? M - r0 : 64;
+    gemm_decode_kernel<<<(unsigned)tiles, kThreads, 0, stream>>>(
+        (int)N, (int)K, (int)m, a.q + r0 * (K / 2), a.s + r0 * (K / 16), a.g, b.q, b.s, b.g,
+        static_cast<uint8_t*>(y) + r0 * ld_y * (int64_t)ysize, y_dtype, ld_y);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nvfp4

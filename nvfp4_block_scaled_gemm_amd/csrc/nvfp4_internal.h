@@ -35,7 +35,7 @@ hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a,
                             PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                             hipStream_t stream);
 
-// gemm_skinny.hip: M <= 32 (decode), K % 256 == 0, N * K / 2 < 4 GiB.
+// gemm_skinny.hip: M <= 128 (decode; 64-row passes), K % 256 == 0, N * K / 2 < 4 GiB.
 hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a,
                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                               hipStream_t stream);

@@ -11,7 +11,7 @@ import torch
 
 import nvfp4_block_scaled_gemm_amd as nv
 import workloads as wl
-from oracle import check_gemm, e4m3_decode, gemm_ref, pack_nibbles
+from oracle import check_gemm, dequantize_ref, e4m3_decode, gemm_ref, pack_nibbles
 from tests.gpu_util import (assert_bytes_equal, need_gpu, note, np_, oracle_global_scale,
                             oracle_quantize, to_gpu)
 
@@ -74,6 +74,61 @@ def test_exhaustive_dequant_identity(M, K):
     y = np_(_gemm(to_gpu(*a), to_gpu(*b), "f32"))
     y_ref, _ = gemm_ref(*a, *b)
     assert np.array_equal(y, y_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("N", [4096, 2048])
+def test_exhaustive_dequant_identity_wide_tiles(N):
+    """A = I_4096 in FP4 (nibble 1.0, scale 1.0, g = 1) against W [N, 4096]
+    whose blocks each hold all 16 nibbles, with every finite scale byte
+    repeated across the blocks: y = W_dq^T exactly.  The tile counts select
+    the 256 x 256 (N = 4096) and 256 x 128 (N = 2048) configurations."""
+    need_gpu()
+    K = M = 4096
+    nib = np.zeros((M, K), dtype=np.uint8)
+    nib[np.arange(M), np.arange(K)] = 0x2
+    a = (pack_nibbles(nib), np.full((M, K // 16), 0x38, np.uint8), np.float32(1))
+    codes = np.arange(256, dtype=np.uint8)
+    codes[0x7F], codes[0xFF] = 0x3F, 0xBF                 # NaN codes replaced
+    rng = np.random.default_rng(N)
+    nblk = N * K // 16
+    perm = np.argsort(rng.random((nblk, 16)), axis=1).astype(np.uint8)   # a permutation per block
+    wn = perm.reshape(N, K)
+    ws = np.resize(np.roll(codes, N // 64), nblk).reshape(N, K // 16)
+    b = (pack_nibbles(wn), ws, np.float32(1))
+    note(f"exhaustive dequant, wide tiles, N={N}")
+    y = np_(_gemm(to_gpu(*a), to_gpu(*b), "f32"))
+    assert np.array_equal(y, dequantize_ref(b[0], b[1]).T.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 16300, 128), (512, 16384, 256), (130, 5000, 384)])
+def test_mid_m_tile_configs(M, N, K):
+    """Shapes whose tile counts pick the 256 x 128 or 128 x 128 configuration
+    (ragged M and N included)."""
+    need_gpu()
+    rng = np.random.default_rng(M + N + K)
+    a = (*_rand_packed(rng, M, K, 0x00, 0x7E), np.float32(0.7))
+    b = (*_rand_packed(rng, N, K, 0x00, 0x7E), np.float32(1.3))
+    note(f"mid-M tile config M={M} N={N} K={K}")
+    y = np_(_gemm(to_gpu(*a), to_gpu(*b), "bf16"))
+    y_ref, bound = gemm_ref(*a, *b)
+    ok, worst = check_gemm(y, y_ref, bound, "bf16")
+    assert ok, worst
+
+
+@pytest.mark.parametrize("M,N", [(65, 96), (100, 40), (128, 200)])
+def test_decode_two_passes(M, N):
+    """65 <= M <= 128 runs the weight-streaming kernel in two 64-row passes."""
+    need_gpu()
+    K = 512
+    rng = np.random.default_rng(M + N)
+    a = (*_rand_packed(rng, M, K, 0x00, 0x7E), np.float32(0.7))
+    b = (*_rand_packed(rng, N, K, 0x00, 0x7E), np.float32(1.3))
+    for out in ("f32", "bf16"):
+        note(f"decode two passes M={M} N={N} out={out}")
+        y = np_(_gemm(to_gpu(*a), to_gpu(*b), out))
+        y_ref, bound = gemm_ref(*a, *b)
+        ok, worst = check_gemm(y, y_ref, bound, out)
+        assert ok, (out, worst)
 
 
 @pytest.mark.parametrize("M", list(range(1, 65)))
