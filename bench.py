@@ -267,13 +267,20 @@ def main():
         else:
             a = nv.nvfp4_quantize(wl.randn((total, k_), wl.seed_for(3, 2), "bf16").to(dev))
         ym = torch.empty((total, n_), dtype=torch.bfloat16, device=dev)
-        timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 10)
-        ms = timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a, (bq, bs, bg), "bf16", y=ym), 20)
-        nbytes = E * n_ * k_ * 9 // 16 + total * k_ * 9 // 16 + total * n_ * 2
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        moe[proj] = {"N": n_, "K": k_, "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
-                     "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "tflops": round(2.0 * total * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
+        runs = [(proj, a, None)]
+        if proj == "gate_up":
+            # the same GEMM reading the token rows through the routing index
+            runs.append(("gate_up_gather", xq, rt.to(torch.int32)))
+        for name, a_op, ri in runs:
+            timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a_op, (bq, bs, bg), "bf16", y=ym,
+                                                  row_index=ri), 10)
+            ms = timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a_op, (bq, bs, bg), "bf16",
+                                                       y=ym, row_index=ri), 20)
+            nbytes = E * n_ * k_ * 9 // 16 + total * k_ * 9 // 16 + total * n_ * 2
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            moe[name] = {"N": n_, "K": k_, "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+                         "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "tflops": round(2.0 * total * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
         del bq, bs, bg, a, ym
 
     # Large outlier workload M = N = K = 16384 (1 % of entries x50): the

@@ -130,6 +130,25 @@ int nvfp4_grouped_gemm(int32_t G, const int32_t* m_offsets, int64_t total_m,
                        const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
                        void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream);
 
+/*
+ * The same grouped GEMM reading its activation rows through an index list
+ * instead of a pre-gathered copy (the routing step of a mixture-of-experts
+ * layer, "The Moment of Synthesis", "The Reasoning Process": tokens are sent
+ * to their experts before the grouped GEMM).  Grouped row r (expert-sorted,
+ * m_offsets as above) multiplies activation row row_index[r] of
+ * a [a_rows, K/2] / [a_rows, K/16]; y [total_m, N] keeps the grouped order.
+ * row_index: DEVICE int32 [total_m]; an index outside [0, a_rows) reads as a
+ * row of zeros.  Indices may repeat (a token routed to several experts).
+ * Otherwise as nvfp4_grouped_gemm (a_rows = total_m and row_index[r] = r give
+ * the same result).  Errors: NVFP4_ERR_INVALID_ARG also for a_rows < 0 or a
+ * null row_index with total_m > 0.
+ */
+int nvfp4_grouped_gemm_gather(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
+                              int64_t total_m, int64_t a_rows, int64_t N, int64_t K,
+                              const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                              const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                              void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ NVFP4_BF16 = 1
 NVFP4_GLOBAL_SCALE_GIVEN = 1
 
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
-            "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm")
+            "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_gather")
 
 _lib = None
 
@@ -59,6 +59,9 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_grouped_gemm.argtypes = [i32, p, i64, i64, i64, p, p, p, p, p, p, p,
                                        ctypes.c_int, i64, p]
     lib.nvfp4_grouped_gemm.restype = ctypes.c_int
+    lib.nvfp4_grouped_gemm_gather.argtypes = [i32, p, p, i64, i64, i64, i64, p, p, p, p, p, p,
+                                              p, ctypes.c_int, i64, p]
+    lib.nvfp4_grouped_gemm_gather.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -107,6 +110,13 @@ def nvfp4_grouped_gemm_raw(G, m_offsets, total_m, N, K, a_q, a_s, a_g, b_q, b_s,
                            y_dtype, ld_y, stream=None) -> int:
     return load().nvfp4_grouped_gemm(G, m_offsets, total_m, N, K, a_q, a_s, a_g, b_q, b_s,
                                      b_g, y, y_dtype, ld_y, _stream(stream))
+
+
+def nvfp4_grouped_gemm_gather_raw(G, m_offsets, row_index, total_m, a_rows, N, K, a_q, a_s,
+                                  a_g, b_q, b_s, b_g, y, y_dtype, ld_y, stream=None) -> int:
+    return load().nvfp4_grouped_gemm_gather(G, m_offsets, row_index, total_m, a_rows, N, K,
+                                            a_q, a_s, a_g, b_q, b_s, b_g, y, y_dtype, ld_y,
+                                            _stream(stream))
 
 
 # --------------------------------------------------------------------------
@@ -158,9 +168,12 @@ def nvfp4_gemm(a, b, out_dtype: str = "bf16", y: torch.Tensor | None = None, str
 
 
 def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: str = "bf16",
-                       y: torch.Tensor | None = None, stream=None):
+                       y: torch.Tensor | None = None, stream=None,
+                       row_index: torch.Tensor | None = None):
     """m_offsets int32 [G+1] (GPU); a = (q [total_m, K/2], s, g [1]);
-    b = (q [G, N, K/2], s [G, N, K/16], g [G]) -> y [total_m, N]."""
+    b = (q [G, N, K/2], s [G, N, K/16], g [G]) -> y [total_m, N].
+    With row_index (int32 [total_m], GPU), grouped row r reads row
+    row_index[r] of a = (q [a_rows, K/2], s, g) instead (no gathered copy)."""
     a_q, a_s, a_g = a
     b_q, b_s, b_g = b
     G, N = b_q.shape[0], b_q.shape[1]
@@ -169,8 +182,16 @@ def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: s
     code, tdt = _DT_OUT[out_dtype]
     if y is None:
         y = torch.empty((total_m, N), dtype=tdt, device=b_q.device)
-    st = nvfp4_grouped_gemm_raw(G, _ptr(m_offsets), total_m, N, K, _ptr(a_q), _ptr(a_s),
-                                _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
-                                y.stride(0), stream)
-    _check("nvfp4_grouped_gemm", st)
+    if row_index is None:
+        st = nvfp4_grouped_gemm_raw(G, _ptr(m_offsets), total_m, N, K, _ptr(a_q), _ptr(a_s),
+                                    _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
+                                    y.stride(0), stream)
+        _check("nvfp4_grouped_gemm", st)
+        return y
+    assert row_index.dtype == torch.int32 and row_index.numel() == total_m
+    st = nvfp4_grouped_gemm_gather_raw(G, _ptr(m_offsets), _ptr(row_index), total_m,
+                                       a_q.shape[0], N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g),
+                                       _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
+                                       y.stride(0), stream)
+    _check("nvfp4_grouped_gemm_gather", st)
     return y

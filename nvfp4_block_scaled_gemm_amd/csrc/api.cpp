@@ -30,6 +30,31 @@ bool tiled_ok(int64_t K, const uint8_t* q, const uint8_t* s, int64_t kmult) {
 // The MFMA tile kernel addresses each operand with 32-bit byte offsets.
 bool offsets32_ok(int64_t rows, int64_t K) { return (rows + 32) * (K / 2) < ((int64_t)1 << 32) - 16; }
 
+// Shared body of the two grouped entry points (row_index == nullptr: rows
+// of A are the grouped rows themselves, a_rows == total_m).
+int grouped_impl(int32_t G, const int32_t* m_offsets, const int32_t* row_index, int64_t total_m,
+                 int64_t a_rows, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+                 const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                 void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {
+  if (G < 0 || total_m < 0 || N < 0 || K < 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (G == 0 && total_m != 0) return NVFP4_ERR_INVALID_ARG;
+  if (total_m > kMaxDim || a_rows > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (total_m == 0 || N == 0) return NVFP4_OK;
+  if (m_offsets == nullptr || y == nullptr || ld_y < N) return NVFP4_ERR_INVALID_ARG;
+  if (!operand_ok(a_rows, K, a_q, a_s, a_g) || !operand_ok(N, K, b_q, b_s, b_g))
+    return NVFP4_ERR_INVALID_ARG;
+  const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
+  hipStream_t st = (hipStream_t)stream;
+  if (K > 0 && tiled_ok(K, a_q, a_s, 512) && tiled_ok(K, b_q, b_s, 512) &&
+      offsets32_ok(total_m, K) && offsets32_ok(a_rows, K) && offsets32_ok(N, K))
+    return from_hip(nvfp4::launch_gemm_grouped(G, m_offsets, row_index, total_m, a_rows, N, K, a,
+                                               b, y, (int)y_dtype, ld_y, st));
+  return from_hip(nvfp4::launch_gemm_grouped_generic(G, m_offsets, row_index, total_m, a_rows, N,
+                                                     K, a, b, y, (int)y_dtype, ld_y, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,22 +127,19 @@ int nvfp4_grouped_gemm(int32_t G, const int32_t* m_offsets, int64_t total_m, int
                        int64_t K, const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
                        const uint8_t* b_q, const uint8_t* b_s, const float* b_g, void* y,
                        nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {
-  if (G < 0 || total_m < 0 || N < 0 || K < 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
-  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
-  if (G == 0 && total_m != 0) return NVFP4_ERR_INVALID_ARG;
-  if (total_m > kMaxDim || N > kMaxDim || K > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
-  if (total_m == 0 || N == 0) return NVFP4_OK;
-  if (m_offsets == nullptr || y == nullptr || ld_y < N) return NVFP4_ERR_INVALID_ARG;
-  if (!operand_ok(total_m, K, a_q, a_s, a_g) || !operand_ok(N, K, b_q, b_s, b_g))
-    return NVFP4_ERR_INVALID_ARG;
-  const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
-  hipStream_t st = (hipStream_t)stream;
-  if (K > 0 && tiled_ok(K, a_q, a_s, 512) && tiled_ok(K, b_q, b_s, 512) &&
-      offsets32_ok(total_m, K) && offsets32_ok(N, K))
-    return from_hip(nvfp4::launch_gemm_grouped(G, m_offsets, total_m, N, K, a, b, y,
-                                               (int)y_dtype, ld_y, st));
-  return from_hip(nvfp4::launch_gemm_grouped_generic(G, m_offsets, total_m, N, K, a, b, y,
-                                                     (int)y_dtype, ld_y, st));
+  return grouped_impl(G, m_offsets, nullptr, total_m, total_m, N, K, a_q, a_s, a_g, b_q, b_s, b_g,
+                      y, y_dtype, ld_y, stream);
+}
+
+int nvfp4_grouped_gemm_gather(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
+                              int64_t total_m, int64_t a_rows, int64_t N, int64_t K,
+                              const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                              const uint8_t* b_q, const uint8_t* b_s, const float* b_g, void* y,
+                              nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {
+  if (a_rows < 0) return NVFP4_ERR_INVALID_ARG;
+  if (total_m > 0 && row_index == nullptr) return NVFP4_ERR_INVALID_ARG;
+  return grouped_impl(G, m_offsets, row_index, total_m, a_rows, N, K, a_q, a_s, a_g, b_q, b_s, b_g,
+                      y, y_dtype, ld_y, stream);
 }
 
 }  // extern "C"

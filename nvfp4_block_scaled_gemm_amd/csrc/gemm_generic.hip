@@ -6,7 +6,9 @@
 // y[m, n] = fl32(ga * gb) * sum_k A(m, k) B(n, k)   (kernelindex "NVFP4 linear
 // layer", description: y = x @ W^T with E2M1 operands and E4M3FN scales per
 // 16 elements).  With m_offsets given, row m uses weight group e where
-// m_offsets[e] <= m < m_offsets[e+1] (grouped form).
+// m_offsets[e] <= m < m_offsets[e+1] (grouped form), and with row_index
+// given it reads activation row row_index[m] (a zero row if that index is
+// outside [0, a_rows)).
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -25,7 +27,8 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
     const uint8_t* __restrict__ a_s, const float* __restrict__ a_g,
     const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
     const float* __restrict__ b_g, const int32_t* __restrict__ m_offsets, int32_t G,
-    void* __restrict__ y, int y_dtype, int64_t ld_y) {
+    const int32_t* __restrict__ row_index, int64_t a_rows, void* __restrict__ y, int y_dtype,
+    int64_t ld_y) {
   const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
   const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
   if (m >= M || n >= N) return;
@@ -40,12 +43,19 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
     e = lo;
   }
   const int64_t nblk = K / 16;
-  const uint8_t* aq = a_q + m * (K / 2);
-  const uint8_t* as = a_s + m * nblk;
+  int64_t src = m;
+  bool a_ok = true;
+  if (row_index != nullptr) {
+    src = row_index[m];
+    a_ok = src >= 0 && src < a_rows;
+    if (!a_ok) src = 0;
+  }
+  const uint8_t* aq = a_q + src * (K / 2);
+  const uint8_t* as = a_s + src * nblk;
   const uint8_t* bq = b_q + (e * N + n) * (K / 2);
   const uint8_t* bs = b_s + (e * N + n) * nblk;
   float acc = 0.0f;
-  for (int64_t blk = 0; blk < nblk; ++blk) {
+  for (int64_t blk = 0; a_ok && blk < nblk; ++blk) {
     int isum = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -61,8 +71,8 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
 }
 
 hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
-                  const int32_t* m_offsets, int32_t G, void* y, int y_dtype, int64_t ld_y,
-                  hipStream_t stream) {
+                  const int32_t* m_offsets, int32_t G, const int32_t* row_index, int64_t a_rows,
+                  void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
   // grid.y is limited to 65535 row tiles; larger M is split into chunks
   const int64_t max_rows = 65535LL * 16;
   for (int64_t m0 = 0; m0 < M; m0 += max_rows) {
@@ -72,6 +82,7 @@ hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperan
     // only through m_offsets, so chunking is used for the dense case alone
     gemm_generic_kernel<<<grid, 256, 0, stream>>>(
         rows, N, K, a.q + m0 * (K / 2), a.s + m0 * (K / 16), a.g, b.q, b.s, b.g, m_offsets, G,
+        row_index, a_rows,
         y_dtype == 0 ? (void*)((float*)y + m0 * ld_y) : (void*)((uint16_t*)y + m0 * ld_y),
         y_dtype, ld_y);
     hipError_t err = hipGetLastError();
@@ -85,14 +96,16 @@ hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperan
 hipError_t launch_gemm_generic(int64_t M, int64_t N, int64_t K, PackedOperand a,
                                PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                                hipStream_t stream) {
-  return launch(M, N, K, a, b, nullptr, 1, y, y_dtype, ld_y, stream);
+  return launch(M, N, K, a, b, nullptr, 1, nullptr, M, y, y_dtype, ld_y, stream);
 }
 
-hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets, int64_t total_m,
+hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets,
+                                       const int32_t* row_index, int64_t total_m, int64_t a_rows,
                                        int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                                        void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
   if (total_m > 65535LL * 16) return hipErrorInvalidValue;
-  return launch(total_m, N, K, a, b, m_offsets, G, y, y_dtype, ld_y, stream);
+  return launch(total_m, N, K, a, b, m_offsets, G, row_index,
+                row_index != nullptr ? a_rows : total_m, y, y_dtype, ld_y, stream);
 }
 
 }  // namespace nvfp4

@@ -96,11 +96,15 @@ struct Cursor {
   int r0, r1;            // the expert's token rows [r0, r1)
   int c0;                // first token row of the current chunk
   int u;                 // current K slice (job) of kJobK elements
+  int rows_c0;           // chunk whose activation rows xq / xs hold (-1: none)
+  uint32_t xq[2], xs[2]; // this lane's activation row offsets per token
+                         // fragment (kOob: no row)
 };
 
 struct Shape {
   int N, nunits, tiles, n_items, stride;
   int64_t total_m;
+  int64_t a_rows;        // rows of the activation operand
 };
 
 // Expert rows of item `it`, clamped into [0, total_m) whatever the offsets
@@ -126,6 +130,7 @@ __device__ __forceinline__ void seek_item(const Shape& sh, const int32_t* __rest
     if (c.r1 > c.r0) {
       c.c0 = c.r0;
       c.u = 0;
+      c.rows_c0 = -1;
       return;
     }
   }
@@ -149,8 +154,12 @@ struct XFrags {
   u32x2 s[2];     // their 8 scale bytes
 };
 
+// GATHER: grouped row r reads activation row row_index[r] (an index outside
+// [0, a_rows) reads as a zero row); otherwise row r itself.
+template <bool GATHER>
 __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
-    Shape sh, const int32_t* __restrict__ m_offsets, int K, const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
+    Shape sh, const int32_t* __restrict__ m_offsets, const int32_t* __restrict__ row_index, int K,
+    const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
     const float* __restrict__ a_g, const uint8_t* __restrict__ b_q,
     const uint8_t* __restrict__ b_s, const float* __restrict__ b_g, void* __restrict__ y,
     int y_dtype, int64_t ld_y) {
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
 
   const uint32_t qrow = (uint32_t)(K / 2), srow = (uint32_t)(K / 16);
   const uint32_t wq_bytes = (uint32_t)sh.N * qrow, ws_bytes = (uint32_t)sh.N * srow;
-  const uint32_t xq_bytes = (uint32_t)sh.total_m * qrow, xs_bytes = (uint32_t)sh.total_m * srow;
+  const uint32_t xq_bytes = (uint32_t)sh.a_rows * qrow, xs_bytes = (uint32_t)sh.a_rows * srow;
   const float ga = a_g[0];
 
   // Load offsets = a per-lane constant + a scalar per job.  Weight nibble
@@ -173,34 +182,58 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
   // Offsets stay in the range-checked vector operand, so weight rows past N
   // read as zero; token rows outside the expert's chunk get an out-of-range
   // offset (zero, and no memory traffic).
-  uint32_t wq_lane[kNibLoads], xq_lane[2], xs_lane[2];
+  uint32_t wq_lane[kNibLoads];
 #pragma unroll
   for (int k = 0; k < kNibLoads; ++k) {
     const uint32_t row = 4u * k + (uint32_t)(lane >> 4);
     wq_lane[k] = row * qrow + (((uint32_t)(lane & 15) ^ (row & 15u)) << 4);
   }
   const uint32_t ws_lane = (uint32_t)(lane >> 1) * srow + (uint32_t)(lane & 1) * 16u;
+
+  // Activation rows of the chunk at c.c0 for this lane's two token
+  // fragments (chunk rows 16g + li), as byte offsets of the row starts.
+  // With GATHER the chunk's 32 indices come through the scalar cache (so
+  // their wait never drains the vector loads) and each lane picks its own.
+  auto chunk_rows = [&](Cursor& c) {
+    int src[2] = {c.c0 + li, c.c0 + 16 + li};
+    if constexpr (GATHER) {
+      const int base = __builtin_amdgcn_readfirstlane(c.c0);
+      const int last = (int)sh.total_m - 1;
+      int v0 = 0, v1 = 0;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    xq_lane[g] = (16u * g + (uint32_t)li) * qrow + (uint32_t)lq * 64u;
-    xs_lane[g] = (16u * g + (uint32_t)li) * srow + (uint32_t)lq * 8u;
-  }
+      for (int j = 0; j < 16; ++j) {
+        const int i0 = row_index[min(base + j, last)], i1 = row_index[min(base + 16 + j, last)];
+        v0 = li == j ? i0 : v0;
+        v1 = li == j ? i1 : v1;
+      }
+      src[0] = v0;
+      src[1] = v1;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bool ok = c.c0 + 16 * g + li < c.r1 && src[g] >= 0 && (int64_t)src[g] < sh.a_rows;
+      c.xq[g] = ok ? (uint32_t)src[g] * qrow : kOob;
+      c.xs[g] = ok ? (uint32_t)src[g] * srow : kOob;
+    }
+    c.rows_c0 = c.c0;
+  };
 
   XFrags xs[kSlots];
 
   // Loads of the job at `c` into slot S: weights to LDS, activations to
   // registers.  Always kLoadsPerJob memory instructions; a finished wave
   // pads with loads of expert 0's first slice.
-  auto issue = [&](const Cursor& c, auto sc) {
+  auto issue = [&](Cursor& c, auto sc) {
     constexpr int S = decltype(sc)::value;
     const bool live = c.item < sh.n_items;
+    if (live && c.rows_c0 != c.c0) chunk_rows(c);  // uniform
     const int e = live ? c.e : 0;
     const uint8_t* wq = b_q + (int64_t)e * sh.N * qrow;
     const uint8_t* ws = b_s + (int64_t)e * sh.N * srow;
     const uint32_t wq_job = live ? (uint32_t)c.n0 * qrow + (uint32_t)c.u * kRowNib : 0u;
     const uint32_t ws_job = live ? (uint32_t)c.n0 * srow + (uint32_t)c.u * kRowSc : 0u;
-    const uint32_t xq_job = (uint32_t)c.c0 * qrow + (uint32_t)c.u * kRowNib;
-    const uint32_t xs_job = (uint32_t)c.c0 * srow + (uint32_t)c.u * kRowSc;
+    const uint32_t xq_job = (uint32_t)c.u * kRowNib + (uint32_t)lq * 64u;
+    const uint32_t xs_job = (uint32_t)c.u * kRowSc + (uint32_t)lq * 8u;
     uint8_t* slot = ring + S * kSlotBytes;
 #pragma unroll
     for (int k = 0; k < kNibLoads; ++k) dma16(wq, wq_bytes, wq_job + wq_lane[k], slot + k * 1024);
@@ -210,11 +243,11 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       // token rows outside the expert's chunk are not fetched at all
-      const bool ok = live && c.c0 + 16 * g + li < c.r1;
-      const uint32_t qo = ok ? xq_job + xq_lane[g] : kOob;
+      const bool ok = live && c.xq[g] != kOob;
+      const uint32_t qo = ok ? c.xq[g] + xq_job : kOob;
 #pragma unroll
       for (int i = 0; i < 4; ++i) xs[S].q[g][i] = ld16(a_q, xq_bytes, ok ? qo + 16u * i : kOob);
-      xs[S].s[g] = ld8(a_s, xs_bytes, ok ? xs_job + xs_lane[g] : kOob);
+      xs[S].s[g] = ld8(a_s, xs_bytes, ok ? c.xs[g] + xs_job : kOob);
     }
   };
 
@@ -301,6 +334,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
 
   Shape shl = sh;
   Cursor lc, cc;
+  lc.rows_c0 = -1;
   seek_item(shl, m_offsets, blockIdx.x * kWaves + wave, lc);
   cc = lc;
   static_for<kSlots - 1>([&](auto sc) {
@@ -327,8 +361,9 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, int64_t total_m, int64_t N,
-                               int64_t K, PackedOperand a, PackedOperand b, void* y, int y_dtype,
+hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
+                               int64_t total_m, int64_t a_rows, int64_t N, int64_t K,
+                               PackedOperand a, PackedOperand b, void* y, int y_dtype,
                                int64_t ld_y, hipStream_t stream) {
   static int num_cu = 0;  // compute units of the current device (one query per process)
   if (num_cu == 0) {
@@ -342,14 +377,19 @@ hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, int64_t tota
   const int64_t n_items = tiles * G;
   if (n_items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int smem = kWaves * kWaveLds;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-  if (attr != hipSuccess) return attr;
+  auto kern = row_index != nullptr ? gemm_grouped_kernel<true> : gemm_grouped_kernel<false>;
+  static const hipError_t attr0 = hipFuncSetAttribute(
+      (const void*)gemm_grouped_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  static const hipError_t attr1 = hipFuncSetAttribute(
+      (const void*)gemm_grouped_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (attr0 != hipSuccess) return attr0;
+  if (attr1 != hipSuccess) return attr1;
   int64_t grid = ((n_items + kWaves - 1) / kWaves);
   if (grid > num_cu) grid = num_cu;  // persistent: one workgroup per CU
-  Shape sh{(int)N, (int)(K / kJobK), (int)tiles, (int)n_items, (int)grid * kWaves, total_m};
-  gemm_grouped_kernel<<<(unsigned)grid, kThreads, smem, stream>>>(sh, m_offsets, (int)K, a.q, a.s, a.g, b.q,
-                                                                  b.s, b.g, y, y_dtype, ld_y);
+  Shape sh{(int)N, (int)(K / kJobK), (int)tiles, (int)n_items, (int)grid * kWaves, total_m,
+           row_index != nullptr ? a_rows : total_m};
+  kern<<<(unsigned)grid, kThreads, smem, stream>>>(sh, m_offsets, row_index, (int)K, a.q, a.s, a.g,
+                                                   b.q, b.s, b.g, y, y_dtype, ld_y);
   return hipGetLastError();
 }
 

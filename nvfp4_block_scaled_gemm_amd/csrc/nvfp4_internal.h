@@ -26,7 +26,10 @@ hipError_t launch_gemm_generic(int64_t M, int64_t N, int64_t K, PackedOperand a,
                                PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                                hipStream_t stream);
 
-hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets, int64_t total_m,
+// row_index (nullptr: none): grouped row r reads activation row row_index[r]
+// of the a_rows rows of `a`; an index outside [0, a_rows) reads as zeros.
+hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets,
+                                       const int32_t* row_index, int64_t total_m, int64_t a_rows,
                                        int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                                        void* y, int y_dtype, int64_t ld_y, hipStream_t stream);
 
@@ -40,9 +43,10 @@ hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a,
                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                               hipStream_t stream);
 
-// gemm_grouped.hip: K % 512 == 0, operands < 4 GiB.
-hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, int64_t total_m,
-                               int64_t N, int64_t K, PackedOperand a, PackedOperand b,
-                               void* y, int y_dtype, int64_t ld_y, hipStream_t stream);
+// gemm_grouped.hip: K % 512 == 0, operands < 4 GiB; row_index as above.
+hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
+                               int64_t total_m, int64_t a_rows, int64_t N, int64_t K,
+                               PackedOperand a, PackedOperand b, void* y, int y_dtype,
+                               int64_t ld_y, hipStream_t stream);
 
 }  // namespace nvfp4

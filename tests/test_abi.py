@@ -138,6 +138,30 @@ def test_grouped_argument_checks(kw, status):
     assert _gg(**kw) == status
 
 
+def _ggx(**kw):
+    args = dict(G=4, m_offsets=P16, row_index=P16, total_m=8, a_rows=5, N=8, K=128, a_q=P16,
+                a_s=P16, a_g=P16, b_q=P16, b_s=P16, b_g=P16, y=P16, y_dtype=nv.NVFP4_BF16, ld_y=8)
+    args.update(kw)
+    order = ("G", "m_offsets", "row_index", "total_m", "a_rows", "N", "K", "a_q", "a_s", "a_g",
+             "b_q", "b_s", "b_g", "y", "y_dtype", "ld_y")
+    return nv.load().nvfp4_grouped_gemm_gather(*[args[k] for k in order], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(row_index=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(a_rows=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(K=40), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(G=0), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(m_offsets=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(a_q=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(a_rows=1 << 31), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(total_m=0, row_index=NULL), nv.NVFP4_OK),
+    (dict(N=0, ld_y=0), nv.NVFP4_OK),
+])
+def test_grouped_gather_argument_checks(kw, status):
+    assert _ggx(**kw) == status
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import nvfp4_block_scaled_gemm_amd._lib as L
     monkeypatch.setattr(L, "_lib", None)

@@ -95,12 +95,49 @@ def test_exhaustive_dequant_identity(counts):
     assert np.array_equal(np_(y), y_ref.astype(np.float32))
 
 
+@pytest.mark.parametrize("counts,N,K,a_rows", [
+    ([3, 0, 5, 1, 0, 40], 96, 512, 50),
+    ([33, 64, 2, 0, 31], 130, 1024, 20),
+    ([7, 9], 40, 768, 12),
+    ([5, 9], 30, 48, 6),
+])
+def test_gather_rows(counts, N, K, a_rows):
+    """Grouped rows read through an index list (duplicates, and two indices
+    outside [0, a_rows) that must read as zero rows) against the oracle on
+    rows gathered on the CPU."""
+    need_gpu()
+    rng = np.random.default_rng(sum(counts) + N + K)
+    G = len(counts)
+    off = wl.ragged_offsets(counts)
+    total = int(off[-1])
+    aq, as_ = _rand_packed(rng, (a_rows,), K)
+    idx = rng.integers(0, a_rows, size=total).astype(np.int32)
+    idx[0], idx[-1] = -1, a_rows + 3
+    ag = np.float32(0.05)
+    bq, bs = _rand_packed(rng, (G, N), K)
+    bg = (rng.random(G) + 0.5).astype(np.float32)
+    valid = (idx >= 0) & (idx < a_rows)
+    gq = np.where(valid[:, None], aq[np.clip(idx, 0, a_rows - 1)], 0).astype(np.uint8)
+    gs = np.where(valid[:, None], as_[np.clip(idx, 0, a_rows - 1)], 0).astype(np.uint8)
+    dev = "cuda"
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)  # noqa: E731
+    y_ref, bound = grouped_gemm_ref(off.numpy(), gq, gs, ag, bq, bs, bg)
+    for out in ("f32", "bf16"):
+        note(f"grouped gather G={G} total={total} a_rows={a_rows} N={N} K={K} out={out}")
+        y = nv.nvfp4_grouped_gemm(off.to(dev), total, (t(aq), t(as_), torch.tensor([ag], device=dev)),
+                                  (t(bq), t(bs), t(bg)), out_dtype=out, row_index=t(idx))
+        torch.cuda.synchronize()
+        ok, worst = check_gemm(np_(y), y_ref, bound, out)
+        assert ok, (out, worst)
+
+
 def test_all_groups_empty_but_last():
     _run([0] * 15 + [4], 64, 512, "f32", seed=3)
 
 
-def _moe_case(proj: str):
-    """MoE workload, one projection: 512 tokens routed top-8 over 256 experts."""
+def _moe_case(proj: str, gather: bool = False):
+    """MoE workload, one projection: 512 tokens routed top-8 over 256 experts
+    (gate_up either on gathered token rows or through the routing index)."""
     need_gpu()
     N, K = wl.MOE_GATE_UP if proj == "gate_up" else wl.MOE_DOWN
     routing = wl.moe_routing(wl.seed_for(3, 0))
@@ -111,12 +148,16 @@ def _moe_case(proj: str):
         x_cpu = wl.randn((wl.MOE_TOKENS, K), wl.seed_for(3, 1), "bf16")
         q, s, g = nv.nvfp4_quantize(x_cpu.cuda())
         rt = routing.row_token.to(dev)
-        a = (q.index_select(0, rt), s.index_select(0, rt), g)
+        if gather:
+            a, row_index = (q, s, g), rt.to(torch.int32)
+        else:
+            a, row_index = (q.index_select(0, rt), s.index_select(0, rt), g), None
         rows_tok = routing.row_token
     else:
         x_cpu = wl.randn((total, K), wl.seed_for(3, 2), "bf16")
         a = nv.nvfp4_quantize(x_cpu.cuda())
         rows_tok = torch.arange(total)
+        row_index = None
     bq = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
     bs = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
     bg = torch.empty((E,), dtype=torch.float32, device=dev)
@@ -126,7 +167,8 @@ def _moe_case(proj: str):
         w = wl.randn((N, K), wseed(e), "bf16", device=dev)
         nv.nvfp4_quantize(w, out=(bq[e], bs[e], bg[e:e + 1]))
     note(f"moe {proj}: grouped gemm")
-    y = nv.nvfp4_grouped_gemm(routing.m_offsets.to(dev), total, a, (bq, bs, bg), "bf16")
+    y = nv.nvfp4_grouped_gemm(routing.m_offsets.to(dev), total, a, (bq, bs, bg), "bf16",
+                              row_index=row_index)
     torch.cuda.synchronize()
     y_np = np_(y)
     ga = oracle_global_scale(x_cpu)
@@ -146,6 +188,10 @@ def _moe_case(proj: str):
 
 def test_moe_gate_up():
     _moe_case("gate_up")
+
+
+def test_moe_gate_up_gather():
+    _moe_case("gate_up", gather=True)
 
 
 def test_moe_down():
