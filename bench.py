@@ -99,15 +99,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of x in the CPU oracle sample (4096 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy", "sweep"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "copy", "mfma_rate"], default="bench",
                     help="copy: a plain 1 GiB device copy, for HBM counter calibration; "
-                         "sweep: the GEMM at growing tile counts (1 .. 1024 workgroups), "
-                         "to see how throughput per CU and the clock change with the "
-                         "number of busy CUs")
+                         "mfma_rate: the sustained fp16 MFMA rate alone and with 4 or 8 "
+                         "dequantisation instructions per MFMA, on one CU and on all of them")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -129,27 +128,40 @@ def main():
                           "bytes_written_per_copy": src.numel() * 4, "copies": args.steps}))
         return
 
-    if args.mode == "sweep":
-        for (M, N, K) in ((256, 256, 8192), (1024, 1024, 8192), (2048, 4096, 8192),
-                          (4096, 4096, 8192), (4096, 8192, 8192), (8192, 8192, 8192)):
-            a = nv.nvfp4_quantize(wl.randn((M, K), 1, "bf16", device=dev))
-            b = nv.nvfp4_quantize(wl.randn((N, K), 2, "bf16", device=dev))
-            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            for _ in range(3):
-                nv.nvfp4_gemm(a, b, "bf16", y=y)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.steps):
-                nv.nvfp4_gemm(a, b, "bf16", y=y)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / args.steps
-            tiles = -(-M // 256) * -(-N // 256)
-            print(json.dumps({"mode": "sweep", "M": M, "N": N, "K": K, "workgroups": tiles,
-                              "us": round(us, 2), "tflops": round(2 * M * N * K / us / 1e6, 1),
-                              "tflops_per_busy_cu": round(2 * M * N * K / us / 1e6 / min(tiles, 256), 3)}),
-                  flush=True)
+    if args.mode == "mfma_rate":
+        import ctypes
+        probe = ctypes.CDLL(os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_probe.so"))
+        probe.probe_mfma_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        stream = torch.cuda.current_stream()
+        for blocks, iters in ((1, 20000), (n_cu, 100000)):
+            out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+            for nv_ops in (0, 4, 8):
+                def launch():
+                    rc = probe.probe_mfma_rate(nv_ops, blocks, 256, iters, out.data_ptr(),
+                                               ctypes.c_void_p(stream.cuda_stream))
+                    assert rc == 0, f"probe_mfma_rate returned {rc}"
+                # all-CU runs first hold the clock for ~30 ms while the power
+                # controller settles, so they warm up longer
+                for _ in range(6 if blocks > 1 else 1):
+                    launch()
+                torch.cuda.synchronize()
+                times = []
+                for _ in range(3):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    launch()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1) * 1e3)
+                us = sorted(times)[1]
+                ns_per_mfma = us * 1e3 / (4 * iters)          # one wave per SIMD
+                busy_cus = min(blocks, n_cu)
+                print(json.dumps({
+                    "mode": "mfma_rate", "workgroups": blocks, "busy_cus": busy_cus,
+                    "valu_per_mfma": nv_ops, "us": round(us, 1),
+                    "ns_per_mfma_per_simd": round(ns_per_mfma, 3),
+                    "tflops": round(busy_cus * 4 * 32768 / ns_per_mfma / 1e3, 1)}), flush=True)
         return
 
     cfg = wl.LINEAR

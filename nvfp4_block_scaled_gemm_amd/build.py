@@ -3,7 +3,9 @@
     python -m nvfp4_block_scaled_gemm_amd.build
 
 Every source compiles to an object under ``_build/`` (in parallel), then one
-shared library is linked next to this file.  Always rebuilds.
+shared library is linked next to this file.  Always rebuilds.  The
+measurement probes under ``probe/`` (used only by ``bench.py``'s probe modes)
+link into a library of their own, ``libnvfp4_probe.so``.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
+PROBE_SRC = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libnvfp4_probe.so")
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of generated code (the device compile
@@ -40,8 +44,14 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+def probe_sources():
+    return sorted(os.path.join(PROBE_SRC, f) for f in os.listdir(PROBE_SRC)
+                  if f.endswith(".hip"))
+
+
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    sub = "probe_" if os.path.dirname(src) == PROBE_SRC else ""
+    obj = os.path.join(BUILD, sub + os.path.basename(src) + ".o")
     cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -51,12 +61,8 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -68,9 +74,19 @@ def build(verbose: bool = False) -> str:
         ctypes.CDLL(tmp)
     except OSError as exc:
         raise RuntimeError(f"built library does not load: {exc}") from exc
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, psrcs = sources(), probe_sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {PROBE_LIB}")
     return LIB
 
 

@@ -147,6 +147,91 @@ struct Cfg {
                 "tile too small for the load split");
 };
 
+// Output tile writer.  acc[i][j] register r holds row 8*(r/4) + 4*(lane/32)
+// + r%4, column lane%32 of its 32x32 tile (row0 / col0: the wave's origin).
+// Whole tiles of an output under 4 GiB have no per-element branches:
+//  * bf16 with 16-byte aligned rows: the wave converts its tile (pairs of
+//    rows in one instruction, round to nearest even) into its own region of
+//    the now idle LDS, reads it back by rows and writes 16 bytes per lane, so
+//    every store fills whole cache lines;
+//  * otherwise buffer stores of single elements, the row offset in a scalar
+//    register and the lane's column offset fixed.
+// Edge tiles check every element.
+template <int DT, int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float alpha, void* y,
+                                           int64_t ld_y, int M, int N, int row0, int col0,
+                                           int lane, bool whole, bool vec, uint32_t y_bytes,
+                                           uint8_t* region) {
+  constexpr int ES = DT == 0 ? 4 : 2;
+  constexpr int TM = FM * 32, TN = FN * 32;
+  const int lg = lane >> 5, li = lane & 31;
+  if (whole && DT == 1 && vec) {
+    constexpr int RS = TN * 2 + 16;  // padded LDS row stride (bytes)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t b = __builtin_bit_cast(
+              uint32_t, __builtin_convertvector(f32x2{acc[i][j][r] * alpha, acc[i][j][r + 1] * alpha}, bf16x2));
+          uint8_t* p = region + row * RS + (j * 32 + li) * 2;
+          *reinterpret_cast<uint16_t*>(p) = (uint16_t)b;
+          *reinterpret_cast<uint16_t*>(p + RS) = (uint16_t)(b >> 16);
+        }
+      }
+    // LDS accesses of one wave complete in order: the reads below see the
+    // writes above
+    constexpr int LPR = TN / 8;            // lanes per row (16 bytes each)
+    constexpr int RPI = 64 / LPR;          // rows per instruction
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)y_bytes, 0x00020000);
+    const int lr = lane / LPR, lc = lane % LPR;
+    const uint32_t voff = (uint32_t)(lr * ld_y + lc * 8) * 2;
+#pragma unroll
+    for (int p = 0; p < TM / RPI; ++p) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + (p * RPI + lr) * RS + lc * 16);
+      const uint32_t soff = ((uint32_t)(row0 + p * RPI) * (uint32_t)ld_y + (uint32_t)col0) * 2;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voff, soff, 0);
+    }
+  } else if (whole) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)y_bytes, 0x00020000);
+    const uint32_t lane_off = (uint32_t)((4 * lg) * ld_y + li) * ES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const uint32_t row = (uint32_t)(row0 + i * 32 + 8 * (r >> 2) + (r & 3));
+        const uint32_t s0 = (row * (uint32_t)ld_y + (uint32_t)col0) * ES;
+        const uint32_t s1 = s0 + (uint32_t)ld_y * ES;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const float v0 = acc[i][j][r] * alpha, v1 = acc[i][j][r + 1] * alpha;
+          if constexpr (DT == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), rsrc, lane_off + j * 32 * ES, s0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), rsrc, lane_off + j * 32 * ES, s1, 0);
+          } else {
+            const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v0, v1}, bf16x2));
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b, rsrc, lane_off + j * 32 * ES, s0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(b >> 16), rsrc, lane_off + j * 32 * ES, s1, 0);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = col0 + j * 32 + li;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (row < M && col < N) store_out(y, (int64_t)row * ld_y + col, acc[i][j][r] * alpha, DT);
+        }
+      }
+  }
+}
+
 // Stage variants of the main loop (4-deep ring):
 //   kFull  - mid-stage sync waits for stage s+1 with one younger stage in
 //            flight, then refills the ring with stage s+3;
@@ -160,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
     int M, int N, int K, const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
     const float* __restrict__ a_g, const uint8_t* __restrict__ b_q,
     const uint8_t* __restrict__ b_s, const float* __restrict__ b_g, void* __restrict__ y,
-    int y_dtype, int64_t ld_y) {
+    int y_dtype, int64_t ld_y, uint32_t y_bytes, int y_flags) {
   static_assert(kStages == 4, "stage modes assume a 4-deep ring");
   using C = Cfg<BM, BN, WAVES_M, WAVES_N>;
   using L = Smem<BM, BN>;
@@ -360,21 +445,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   if (s + 1 < nstage) run_stage(s++, std::integral_constant<StageMode, kTail0>{});
   run_stage(s, std::integral_constant<StageMode, kLast>{});
 
-  // ---- epilogue: y = fl32(ga * gb) * acc.  acc[i][j] reg r holds row
-  // 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of its 32x32 tile.
+  // ---- epilogue: y = fl32(ga * gb) * acc.  The ring is idle once every
+  // wave has finished its last stage; each wave then owns a region of it.
   const float alpha = a_g[0] * b_g[0];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * C::TN + j * 32 + li;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (row < M && col < N)
-          store_out(y, (int64_t)row * ld_y + col, acc[i][j][r] * alpha, y_dtype);
-      }
-    }
+  const bool whole = y_bytes != 0 && m0 + BM <= M && n0 + BN <= N;
+  const bool vec = (y_flags & 1) != 0;
+  const int row0 = m0 + wm * C::TM, col0 = n0 + wn * C::TN;
+  constexpr int kRegion = C::TM * (C::TN * 2 + 16);
+  static_assert(C::kWaves * kRegion <= kStages * L::kBytes, "epilogue staging exceeds the ring");
+  workgroup_barrier();
+  uint8_t* region = smem + wave * kRegion;
+  if (y_dtype == 0)
+    store_tile<0>(acc, alpha, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
+  else
+    store_tile<1>(acc, alpha, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -390,8 +474,15 @@ hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOp
   if (attr != hipSuccess) return attr;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // extent of y in bytes when below 4 GiB (whole tiles then use 32-bit
+  // buffer offsets), else 0 (every tile takes the checked writer)
+  const int64_t extent = ((M - 1) * ld_y + N) * (y_dtype == 0 ? 4 : 2);
+  const uint32_t y_bytes = extent < (int64_t)0xFFFFFFFF ? (uint32_t)extent : 0u;
+  // bit 0: rows start on 16-byte boundaries (16-byte stores of bf16 rows)
+  const int y_flags = ((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ld_y % 8 == 0) ? 1 : 0;
   kern<<<(unsigned)tiles, C::kThreads, smem, stream>>>((int)M, (int)N, (int)K, a.q, a.s, a.g,
-                                                        b.q, b.s, b.g, y, y_dtype, ld_y);
+                                                        b.q, b.s, b.g, y, y_dtype, ld_y, y_bytes,
+                                                        y_flags);
   return hipGetLastError();
 }
 

@@ -247,3 +247,33 @@ def test_large_outlier_workload_sampled():
     y_ref, bound = gemm_ref(*ra, *rb)
     ok, worst = check_gemm(np_(y)[np.ix_(rows, cols)], y_ref, bound, "bf16")
     assert ok, worst
+
+
+@pytest.mark.parametrize("out,pad,shift", [("bf16", 8, 0), ("bf16", 3, 0), ("bf16", 8, 1),
+                                           ("f32", 5, 0), ("f32", 4, 1)])
+def test_strided_output_writers(out, pad, shift):
+    """y written into a wider buffer (row stride N + pad, start shifted by
+    `shift` elements): whole 256 x 256 tiles take the staged 16-byte writer
+    (bf16, 16-byte aligned rows) or the per-element one (odd stride, shifted
+    start, fp32), edge tiles the checked one; the padding keeps its
+    sentinel."""
+    need_gpu()
+    M, N, K = 4096 + 40, 4096 + 24, 128
+    rng = np.random.default_rng(pad * 10 + shift)
+    a = (*_rand_packed(rng, M, K, 0x20, 0x48), np.float32(0.5))
+    b = (*_rand_packed(rng, N, K, 0x20, 0x48), np.float32(0.25))
+    code_dt = torch.bfloat16 if out == "bf16" else torch.float32
+    ld = N + pad
+    buf = torch.full((M * ld + shift + pad,), -7.0, dtype=code_dt, device="cuda")
+    y = buf[shift:shift + M * ld].view(M, ld)[:, :N]
+    note(f"strided output out={out} ld_y={ld} shift={shift}")
+    nv.nvfp4_gemm(to_gpu(*a), to_gpu(*b), out_dtype=out, y=y)
+    torch.cuda.synchronize()
+    y_ref, bound = gemm_ref(*a, *b)
+    ok, worst = check_gemm(np_(y.contiguous()), y_ref, bound, out)
+    assert ok, worst
+    full = buf.float().cpu().numpy()
+    mask = np.ones(full.shape, bool)
+    idx = shift + (np.arange(M)[:, None] * ld + np.arange(N)[None, :])
+    mask[idx.ravel()] = False
+    assert np.all(full[mask] == -7.0), "writes outside the output view"
