@@ -34,7 +34,7 @@
 //    sides).  Each token fragment is dequantised once per step and reused by
 //    the four weight fragments.
 //  * After the last slice of an item-chunk the wave scales by ga * gb[e] and
-//    stores its 64 x ntok outputs.
+//    stores its 64 x ntok outputs, four consecutive columns per store.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -105,6 +105,8 @@ struct Shape {
   int N, nunits, tiles, n_items, stride;
   int64_t total_m;
   int64_t a_rows;        // rows of the activation operand
+  uint32_t y_bytes;      // extent of y when below 4 GiB and its rows take
+                         // 8-byte (bf16) / 16-byte (fp32) stores, else 0
 };
 
 // Expert rows of item `it`, clamped into [0, total_m) whatever the offsets
@@ -316,19 +318,44 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
     if (c.u == sh.nunits - 1) {
       // acc[f][g] reg r: weight row n0 + 16f + 4*lq + r, token c0 + 16g + li
       const float alpha = ga * b_g[c.e];
-#pragma unroll
-      for (int f = 0; f < kFrags; ++f)
+      if (sh.y_bytes != 0 && c.n0 + kRows <= sh.N) {  // uniform
+        // the lane's four consecutive outputs of a token in one store;
+        // tokens outside the chunk get an offset past the output (no write)
+        const auto ry = rsrc(y, sh.y_bytes);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const int tok = 16 * g + li;
+          const uint32_t row_off = (uint32_t)(c.c0 + tok) * (uint32_t)ld_y;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int n = c.n0 + 16 * f + 4 * lq + r;
-            if (tok < ntok && n < sh.N)
-              store_out(y, (int64_t)(c.c0 + tok) * ld_y + n, acc[f][g][r] * alpha, y_dtype);
+          for (int f = 0; f < kFrags; ++f) {
+            const uint32_t el = row_off + (uint32_t)(c.n0 + 16 * f + 4 * lq);
+            const f32x4 v = acc[f][g] * alpha;
+            if (y_dtype == 0) {
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry,
+                                                     tok < ntok ? el * 4u : kOob, 0, 0);
+            } else {
+              const u32x2 b = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2)),
+                               __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2))};
+              __builtin_amdgcn_raw_buffer_store_b64(b, ry, tok < ntok ? el * 2u : kOob, 0, 0);
+            }
+            acc[f][g] = f32x4{0, 0, 0, 0};
           }
-          acc[f][g] = f32x4{0, 0, 0, 0};
         }
+      } else {
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int tok = 16 * g + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int n = c.n0 + 16 * f + 4 * lq + r;
+              if (tok < ntok && n < sh.N)
+                store_out(y, (int64_t)(c.c0 + tok) * ld_y + n, acc[f][g][r] * alpha, y_dtype);
+            }
+            acc[f][g] = f32x4{0, 0, 0, 0};
+          }
+      }
     }
   };
 
@@ -386,8 +413,14 @@ hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_
   if (attr1 != hipSuccess) return attr1;
   int64_t grid = ((n_items + kWaves - 1) / kWaves);
   if (grid > num_cu) grid = num_cu;  // persistent: one workgroup per CU
+  // whole 4-column groups of a row go out in one store when the rows are
+  // aligned for it and the output's byte extent fits 32-bit offsets
+  const int es = y_dtype == 0 ? 4 : 2;
+  const int64_t extent = total_m > 0 ? ((total_m - 1) * ld_y + N) * es : 0;
+  const bool aligned = (reinterpret_cast<uintptr_t>(y) % (4 * es)) == 0 && ld_y % 4 == 0;
+  const uint32_t y_bytes = aligned && extent < (int64_t)0xFFFFFFF0 ? (uint32_t)extent : 0u;
   Shape sh{(int)N, (int)(K / kJobK), (int)tiles, (int)n_items, (int)grid * kWaves, total_m,
-           row_index != nullptr ? a_rows : total_m};
+           row_index != nullptr ? a_rows : total_m, y_bytes};
   kern<<<(unsigned)grid, kThreads, smem, stream>>>(sh, m_offsets, row_index, (int)K, a.q, a.s, a.g,
                                                    b.q, b.s, b.g, y, y_dtype, ld_y);
   return hipGetLastError();

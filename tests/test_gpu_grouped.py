@@ -196,3 +196,38 @@ def test_moe_gate_up_gather():
 
 def test_moe_down():
     _moe_case("down")
+
+
+@pytest.mark.parametrize("out,pad,shift", [("bf16", 4, 0), ("bf16", 1, 0), ("bf16", 4, 2),
+                                           ("f32", 8, 0), ("f32", 4, 1)])
+def test_strided_output(out, pad, shift):
+    """y inside a wider buffer (row stride N + pad, start shifted by `shift`
+    elements): aligned rows take the four-column stores, the others the
+    per-element writer; the padding keeps its sentinel."""
+    need_gpu()
+    counts, N, K = [33, 0, 2, 31, 16, 40], 200, 512
+    rng = np.random.default_rng(pad * 10 + shift)
+    G = len(counts)
+    off = wl.ragged_offsets(counts)
+    total = int(off[-1])
+    aq, as_ = _rand_packed(rng, (total,), K)
+    ag = np.float32(0.05)
+    bq, bs = _rand_packed(rng, (G, N), K)
+    bg = (rng.random(G) + 0.5).astype(np.float32)
+    dev = "cuda"
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)  # noqa: E731
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    ld = N + pad
+    buf = torch.full((total * ld + shift + pad,), -7.0, dtype=dt, device=dev)
+    y = buf[shift:shift + total * ld].view(total, ld)[:, :N]
+    note(f"grouped strided output out={out} ld_y={ld} shift={shift}")
+    nv.nvfp4_grouped_gemm(off.to(dev), total, (t(aq), t(as_), torch.tensor([ag], device=dev)),
+                          (t(bq), t(bs), t(bg)), out_dtype=out, y=y)
+    torch.cuda.synchronize()
+    y_ref, bound = grouped_gemm_ref(off.numpy(), aq, as_, ag, bq, bs, bg)
+    ok, worst = check_gemm(np_(y.contiguous()), y_ref, bound, out)
+    assert ok, worst
+    full = buf.float().cpu().numpy()
+    mask = np.ones(full.shape, bool)
+    mask[(shift + np.arange(total)[:, None] * ld + np.arange(N)[None, :]).ravel()] = False
+    assert np.all(full[mask] == -7.0), "writes outside the output view"
