@@ -234,7 +234,7 @@ def main():
         # back-to-back launches between one pair of events (a decode step
         # issues its GEMMs back to back); per-launch events would add their
         # own overhead to a ~10 us kernel
-        timed_batch(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 16)
+        timed_batch(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 256)
         ms = timed_batch(lambda i: nv.nvfp4_gemm(xd, copies[i % 16], "bf16", y=yd), 128)
         nbytes = dcfg.N * dcfg.K * 9 // 16 + m * dcfg.K * 9 // 16 + m * dcfg.N * 2
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -284,8 +284,9 @@ def main():
             # the same GEMM reading the token rows through the routing index
             runs.append(("gate_up_gather", xq, rt.to(torch.int32)))
         for name, a_op, ri in runs:
+            # ~20-30 ms of untimed launches first: clocks settle under a new load
             timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a_op, (bq, bs, bg), "bf16", y=ym,
-                                                  row_index=ri), 10)
+                                                  row_index=ri), 40)
             ms = timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a_op, (bq, bs, bg), "bf16",
                                                        y=ym, row_index=ri), 20)
             nbytes = E * n_ * k_ * 9 // 16 + total * k_ * 9 // 16 + total * n_ * 2
