@@ -226,6 +226,47 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    # The linear GEMM writing its output as NVFP4 (the next layer's input
+    # quantised in the epilogue, static global scale) against the unfused
+    # pair: bf16 GEMM, then the quantiser on that output with the same scale.
+    y32 = nv.nvfp4_gemm(xq, wq, "f32")
+    yg = (y32.abs().max() / 2688.0).reshape(1).float()
+    del y32
+    fq = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    fs = torch.empty((M, N // 16), dtype=torch.uint8, device=dev)
+    uq, us_, ug = torch.empty_like(fq), torch.empty_like(fs), torch.empty(1, device=dev)
+    timed(lambda i: nv.nvfp4_gemm_nvfp4_out(xq, wq, yg, out=(fq, fs)), 40)
+    fused_ms = timed(lambda i: nv.nvfp4_gemm_nvfp4_out(xq, wq, yg, out=(fq, fs)), 20)
+
+    def unfused(i):
+        nv.nvfp4_gemm(xq, wq, "bf16", y=y)
+        nv.nvfp4_quantize(y, global_scale=yg, out=(uq, us_, ug))
+    timed(unfused, 20)
+    unfused_ms = timed(unfused, 20)
+    # decode-sized output (16 tokens): the separate quantiser is a launch of
+    # its own for a 256 KB tensor; back to back, weights as above
+    x16 = nv.nvfp4_quantize(wl.randn((16, K), wl.seed_for(2, 0), "bf16").to(dev))
+    y16 = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
+    f16q = torch.empty((16, N // 2), dtype=torch.uint8, device=dev)
+    f16s = torch.empty((16, N // 16), dtype=torch.uint8, device=dev)
+    u16q, u16s, u16g = torch.empty_like(f16q), torch.empty_like(f16s), torch.empty(1, device=dev)
+    timed_batch(lambda i: nv.nvfp4_gemm_nvfp4_out(x16, wq, yg, out=(f16q, f16s)), 64)
+    fused16_ms = timed_batch(lambda i: nv.nvfp4_gemm_nvfp4_out(x16, wq, yg, out=(f16q, f16s)), 128)
+
+    def unfused16(i):
+        nv.nvfp4_gemm(x16, wq, "bf16", y=y16)
+        nv.nvfp4_quantize(y16, global_scale=yg, out=(u16q, u16s, u16g))
+    timed_batch(unfused16, 64)
+    unfused16_ms = timed_batch(unfused16, 128)
+    fused = {"workload": f"linear_m{M}_n{N}_k{K}, NVFP4 output, static global scale",
+             "decode_m16_fused_us": round(fused16_ms * 1e3, 2),
+             "decode_m16_unfused_us": round(unfused16_ms * 1e3, 2),
+             "fused_us": round(fused_ms * 1e3, 2),
+             "fused_tflops": round(2.0 * M * N * K / (fused_ms * 1e-3) / 1e12, 1),
+             "unfused_gemm_bf16_then_quantize_us": round(unfused_ms * 1e3, 2),
+             "output_bytes_fused": M * N * 9 // 16,
+             "output_bytes_unfused": M * N * 2 + 2 * M * N + M * N * 9 // 16}
+
     decode = {}
     for m in (1, 16, 32):
         dcfg = wl.DECODE[m]
@@ -347,6 +388,7 @@ def main():
                        weights="16 rotating copies (cache-cold)"),
         "moe_grouped": dict(moe, peak_GBps=PEAK_HBM_GBS),
         "large": large,
+        "fused_quant_out": fused,
         "mid_m": dict(mid_m, workload="m{64..1024}_n8192_k8192, 16 rotating weight copies"),
     }
     if not args.no_cpu_baseline:

@@ -110,6 +110,28 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K,
                void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream);
 
 /*
+ * Dense NVFP4 GEMM whose output is NVFP4 again: the next layer's input
+ * quantisation done in this GEMM's epilogue with a static global scale fixed
+ * ahead of time (leverageai "blackwell-nvfp4-gemm-optimization", "What is
+ * this?": quantisation may happen before execution), so y never makes a
+ * round trip through HBM in a wide type.
+ *   y[m, n] = the fp32 value nvfp4_gemm stores with y_dtype NVFP4_F32
+ *   (y_q, y_s) = the encoding of y by nvfp4_quantize's steps with g = *y_g
+ *                (the bytes nvfp4_quantize with NVFP4_GLOBAL_SCALE_GIVEN
+ *                would write from that fp32 y, exactly)
+ * y_q [M, N/2] and y_s [M, N/16] are dense (row strides N/2 and N/16
+ * bytes); y_q is 8-byte aligned.  y_g is a DEVICE fp32 scalar, read only;
+ * it must be finite and >= 0 (0 gives scale bytes 0 and magnitude codes 0).
+ * Values whose magnitude exceeds 2688 * g saturate (scale 448, code 6).
+ * N % 16 == 0 (NVFP4_ERR_INVALID_ARG otherwise); the other requirements and
+ * the kernel dispatch are those of nvfp4_gemm.
+ */
+int nvfp4_gemm_nvfp4_out(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                         const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                         uint8_t* y_q, uint8_t* y_s, const float* y_g, void* stream);
+
+/*
  * Grouped (per-expert) NVFP4 GEMM for mixture-of-experts layers whose
  * experts each see a small, uneven number of tokens (magik.net "The Moment
  * of Synthesis", "The Reasoning Process": grouped GEMM is the lever for tiny

@@ -24,7 +24,8 @@ NVFP4_BF16 = 1
 NVFP4_GLOBAL_SCALE_GIVEN = 1
 
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
-            "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_gather")
+            "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_nvfp4_out", "nvfp4_grouped_gemm",
+            "nvfp4_grouped_gemm_gather")
 
 _lib = None
 
@@ -56,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_quantize.restype = ctypes.c_int
     lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, ctypes.c_int, i64, p]
     lib.nvfp4_gemm.restype = ctypes.c_int
+    lib.nvfp4_gemm_nvfp4_out.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p]
+    lib.nvfp4_gemm_nvfp4_out.restype = ctypes.c_int
     lib.nvfp4_grouped_gemm.argtypes = [i32, p, i64, i64, i64, p, p, p, p, p, p, p,
                                        ctypes.c_int, i64, p]
     lib.nvfp4_grouped_gemm.restype = ctypes.c_int
@@ -104,6 +107,12 @@ def nvfp4_gemm_raw(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y, y_dtype, ld_y,
                    stream=None) -> int:
     return load().nvfp4_gemm(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y, y_dtype, ld_y,
                              _stream(stream))
+
+
+def nvfp4_gemm_nvfp4_out_raw(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y_q, y_s, y_g,
+                             stream=None) -> int:
+    return load().nvfp4_gemm_nvfp4_out(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y_q, y_s, y_g,
+                                       _stream(stream))
 
 
 def nvfp4_grouped_gemm_raw(G, m_offsets, total_m, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y,
@@ -165,6 +174,25 @@ def nvfp4_gemm(a, b, out_dtype: str = "bf16", y: torch.Tensor | None = None, str
                         _ptr(b_g), _ptr(y), code, y.stride(0), stream)
     _check("nvfp4_gemm", st)
     return y
+
+
+def nvfp4_gemm_nvfp4_out(a, b, y_g: torch.Tensor, out=None, stream=None):
+    """a = (q, s, g) of x [M, K], b = (q, s, g) of W [N, K]; y_g = the output's
+    static global scale (fp32 [1], GPU) -> (q [M, N/2], s [M, N/16], y_g): y
+    quantised in the GEMM's epilogue.  ``out`` = (q, s) reuses buffers."""
+    a_q, a_s, a_g = a
+    b_q, b_s, b_g = b
+    M, N, K = a_q.shape[0], b_q.shape[0], a_q.shape[1] * 2
+    assert b_q.shape[1] * 2 == K and y_g.dtype == torch.float32 and y_g.numel() == 1
+    if out is None:
+        q = torch.empty((M, N // 2), dtype=torch.uint8, device=a_q.device)
+        s = torch.empty((M, N // 16), dtype=torch.uint8, device=a_q.device)
+    else:
+        q, s = out
+    st = nvfp4_gemm_nvfp4_out_raw(M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q),
+                                  _ptr(b_s), _ptr(b_g), _ptr(q), _ptr(s), _ptr(y_g), stream)
+    _check("nvfp4_gemm_nvfp4_out", st)
+    return q, s, y_g
 
 
 def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: str = "bf16",

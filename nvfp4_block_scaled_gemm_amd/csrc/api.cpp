@@ -55,6 +55,22 @@ int grouped_impl(int32_t G, const int32_t* m_offsets, const int32_t* row_index, 
                                                      K, a, b, y, (int)y_dtype, ld_y, st));
 }
 
+// Shape dispatch of the dense GEMM (both entry points, so an NVFP4 output
+// sees exactly the fp32 values of the fp32 output).  dt 2: NVFP4 output qo.
+int gemm_dispatch(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+                  const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                  void* y, int dt, int64_t ld_y, nvfp4::QuantOut qo, hipStream_t st) {
+  const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
+  // K == 0: the sum is empty; the general kernel writes zeros.
+  if (K > 0 && M <= 128 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256) &&
+      offsets32_ok(N, K))
+    return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st, qo));
+  if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128) &&
+      offsets32_ok(M, K) && offsets32_ok(N, K))
+    return from_hip(nvfp4::launch_gemm_mfma(M, N, K, a, b, y, dt, ld_y, st, qo));
+  return from_hip(nvfp4::launch_gemm_generic(M, N, K, a, b, y, dt, ld_y, st, qo));
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,17 +126,24 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_
   if (y == nullptr || ld_y < N) return NVFP4_ERR_INVALID_ARG;
   if (!operand_ok(M, K, a_q, a_s, a_g) || !operand_ok(N, K, b_q, b_s, b_g))
     return NVFP4_ERR_INVALID_ARG;
-  const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
-  hipStream_t st = (hipStream_t)stream;
-  const int dt = (int)y_dtype;
-  // K == 0: the sum is empty; the general kernel writes zeros.
-  if (K > 0 && M <= 128 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256) &&
-      offsets32_ok(N, K))
-    return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st));
-  if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128) &&
-      offsets32_ok(M, K) && offsets32_ok(N, K))
-    return from_hip(nvfp4::launch_gemm_mfma(M, N, K, a, b, y, dt, ld_y, st));
-  return from_hip(nvfp4::launch_gemm_generic(M, N, K, a, b, y, dt, ld_y, st));
+  return gemm_dispatch(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y, (int)y_dtype, ld_y,
+                       nvfp4::QuantOut{}, (hipStream_t)stream);
+}
+
+int nvfp4_gemm_nvfp4_out(int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
+                         const uint8_t* a_s, const float* a_g, const uint8_t* b_q,
+                         const uint8_t* b_s, const float* b_g, uint8_t* y_q, uint8_t* y_s,
+                         const float* y_g, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 16 != 0 || N % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
+  if (y_g == nullptr) return NVFP4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (y_q == nullptr || y_s == nullptr) return NVFP4_ERR_INVALID_ARG;
+  if (!operand_ok(M, K, a_q, a_s, a_g) || !operand_ok(N, K, b_q, b_s, b_g))
+    return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(y_q, 8)) return NVFP4_ERR_UNSUPPORTED;
+  return gemm_dispatch(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, nullptr, 2, N,
+                       nvfp4::QuantOut{y_q, y_s, y_g}, (hipStream_t)stream);
 }
 
 int nvfp4_grouped_gemm(int32_t G, const int32_t* m_offsets, int64_t total_m, int64_t N,

@@ -8,8 +8,10 @@
 // 16 elements).  With m_offsets given, row m uses weight group e where
 // m_offsets[e] <= m < m_offsets[e+1] (grouped form), and with row_index
 // given it reads activation row row_index[m] (a zero row if that index is
-// outside [0, a_rows)).
+// outside [0, a_rows)).  With NVFP4 output (dense form only) the same fp32
+// values are quantised in 16-column blocks by the quantiser's encoder.
 #include "nvfp4_device.h"
+#include "nvfp4_encode.h"
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
@@ -22,16 +24,16 @@ __device__ __forceinline__ int e2m1_x2(uint32_t nib) {
   return (nib & 8u) ? -mag : mag;
 }
 
-__global__ __launch_bounds__(256) void gemm_generic_kernel(
-    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_q,
-    const uint8_t* __restrict__ a_s, const float* __restrict__ a_g,
-    const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
-    const float* __restrict__ b_g, const int32_t* __restrict__ m_offsets, int32_t G,
-    const int32_t* __restrict__ row_index, int64_t a_rows, void* __restrict__ y, int y_dtype,
-    int64_t ld_y) {
-  const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
-  const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
-  if (m >= M || n >= N) return;
+// One output y[m, n] (fp32, scaled).
+__device__ __forceinline__ float dot(int64_t M, int64_t N, int64_t K,
+                                     const uint8_t* __restrict__ a_q,
+                                     const uint8_t* __restrict__ a_s,
+                                     const uint8_t* __restrict__ b_q,
+                                     const uint8_t* __restrict__ b_s,
+                                     const int32_t* __restrict__ m_offsets, int32_t G,
+                                     const int32_t* __restrict__ row_index, int64_t a_rows,
+                                     int64_t m, int64_t n, const float* __restrict__ a_g,
+                                     const float* __restrict__ b_g) {
   int64_t e = 0;
   if (m_offsets != nullptr) {
     // last group e with m_offsets[e] <= m (non-decreasing offsets)
@@ -67,12 +69,53 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
     acc += sc * ((float)isum * 0.25f);                                 // exact term
   }
   const float alpha = a_g[0] * b_g[e];
-  store_out(y, m * ld_y + n, acc * alpha, y_dtype);
+  return acc * alpha;
+}
+
+__global__ __launch_bounds__(256) void gemm_generic_kernel(
+    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_q,
+    const uint8_t* __restrict__ a_s, const float* __restrict__ a_g,
+    const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
+    const float* __restrict__ b_g, const int32_t* __restrict__ m_offsets, int32_t G,
+    const int32_t* __restrict__ row_index, int64_t a_rows, void* __restrict__ y, int y_dtype,
+    int64_t ld_y, QuantOut qo) {
+  const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
+  const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
+  const bool in = m < M && n < N;
+  if (!in && y_dtype != 2) return;  // the NVFP4 writer needs every thread at its barrier
+  const float v = in ? dot(M, N, K, a_q, a_s, b_q, b_s, m_offsets, G, row_index, a_rows, m, n,
+                           a_g, b_g)
+                     : 0.0f;
+  if (y_dtype != 2) {
+    store_out(y, m * ld_y + n, v, y_dtype);
+    return;
+  }
+  // NVFP4 output: the workgroup's 16 x 16 values go through LDS; thread t < 16
+  // encodes row t's 16-column block with the given global scale
+  __shared__ float tile[16][17];
+  tile[threadIdx.x >> 4][threadIdx.x & 15] = v;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int64_t row = (int64_t)blockIdx.y * 16 + threadIdx.x, c0 = (int64_t)blockIdx.x * 16;
+    const float g = qo.g[0];
+    const enc::EncodeParams P = enc::make_params(g);
+    const int mode = enc::encode_mode(g);
+    enc::Block16 b;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) b.v[e] = tile[threadIdx.x][e];
+    if (row < M && c0 < N) {
+      uint8_t* qp = qo.q + row * (N / 2) + c0 / 2;
+      uint8_t* sp = qo.s + row * (N / 16) + c0 / 16;
+      if (mode == 1) enc::encode_block<1>(b, P, qp, sp);
+      else if (mode == 0) enc::encode_block<0>(b, P, qp, sp);
+      else enc::encode_block<2>(b, P, qp, sp);
+    }
+  }
 }
 
 hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                   const int32_t* m_offsets, int32_t G, const int32_t* row_index, int64_t a_rows,
-                  void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
+                  void* y, int y_dtype, int64_t ld_y, hipStream_t stream, QuantOut qo) {
   // grid.y is limited to 65535 row tiles; larger M is split into chunks
   const int64_t max_rows = 65535LL * 16;
   for (int64_t m0 = 0; m0 < M; m0 += max_rows) {
@@ -80,11 +123,17 @@ hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperan
     dim3 grid((unsigned)((N + 15) / 16), (unsigned)((rows + 15) / 16));
     // chunks past the first shift A and y; the group search sees global rows
     // only through m_offsets, so chunking is used for the dense case alone
+    QuantOut qc = qo;
+    if (y_dtype == 2) {
+      qc.q += m0 * (N / 2);
+      qc.s += m0 * (N / 16);
+    }
     gemm_generic_kernel<<<grid, 256, 0, stream>>>(
         rows, N, K, a.q + m0 * (K / 2), a.s + m0 * (K / 16), a.g, b.q, b.s, b.g, m_offsets, G,
         row_index, a_rows,
-        y_dtype == 0 ? (void*)((float*)y + m0 * ld_y) : (void*)((uint16_t*)y + m0 * ld_y),
-        y_dtype, ld_y);
+        y_dtype == 2 ? y
+                     : (y_dtype == 0 ? (void*)((float*)y + m0 * ld_y) : (void*)((uint16_t*)y + m0 * ld_y)),
+        y_dtype, ld_y, qc);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -95,8 +144,8 @@ hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperan
 
 hipError_t launch_gemm_generic(int64_t M, int64_t N, int64_t K, PackedOperand a,
                                PackedOperand b, void* y, int y_dtype, int64_t ld_y,
-                               hipStream_t stream) {
-  return launch(M, N, K, a, b, nullptr, 1, nullptr, M, y, y_dtype, ld_y, stream);
+                               hipStream_t stream, QuantOut qo) {
+  return launch(M, N, K, a, b, nullptr, 1, nullptr, M, y, y_dtype, ld_y, stream, qo);
 }
 
 hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets,
@@ -105,7 +154,7 @@ hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets,
                                        void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
   if (total_m > 65535LL * 16) return hipErrorInvalidValue;
   return launch(total_m, N, K, a, b, m_offsets, G, row_index,
-                row_index != nullptr ? a_rows : total_m, y, y_dtype, ld_y, stream);
+                row_index != nullptr ? a_rows : total_m, y, y_dtype, ld_y, stream, QuantOut{});
 }
 
 }  // namespace nvfp4

@@ -27,6 +27,7 @@
 //    the 8 XCDs, so each XCD is given a compact block of output tiles whose
 //    A and B rows it shares in its own L2.
 #include "nvfp4_device.h"
+#include "nvfp4_encode.h"
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
@@ -232,6 +233,56 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float al
   }
 }
 
+// NVFP4 output tile: the fp32 values fl32(alpha * acc) that the fp32 writer
+// would store are staged by rows in the wave's LDS region (half the wave
+// tile per pass), and each lane then encodes whole 16-column blocks with the
+// quantiser's exact block encoder, given the output's global scale.
+template <int kMode, int FM, int FN>
+__device__ __forceinline__ void quant_tile(const f32x16 (&acc)[FM][FN], float alpha, int M, int N,
+                                           int row0, int col0, int lane, uint8_t* region,
+                                           const QuantOut& qo, const enc::EncodeParams& P) {
+  constexpr int TN = FN * 32;
+  constexpr int PF = FM >= 2 ? FM / 2 : 1;  // fragment rows per pass
+  constexpr int PR = PF * 32;               // tile rows per pass
+  constexpr int RS = TN * 4 + 16;           // padded LDS row stride (bytes)
+  constexpr int BPR = TN / 16;              // 16-column blocks per row
+  constexpr int NB = PR * BPR;              // blocks per pass
+  static_assert(NB % 64 == 0, "whole blocks per lane");
+  const int lg = lane >> 5, li = lane & 31;
+  const int64_t qld = N / 2, sld = N / 16;
+#pragma unroll
+  for (int pass = 0; pass < FM / PF; ++pass) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+          *reinterpret_cast<float*>(region + row * RS + (j * 32 + li) * 4) =
+              acc[pass * PF + i][j][r] * alpha;
+        }
+    // LDS accesses of one wave complete in order: the reads below see the
+    // writes above, and the next pass's writes follow these reads
+#pragma unroll
+    for (int t = 0; t < NB / 64; ++t) {
+      const int blk = t * 64 + lane, row = blk / BPR, cb = blk % BPR;
+      const int grow = row0 + pass * PR + row, gcol = col0 + cb * 16;
+      enc::Block16 b;
+      const u32x4* src = reinterpret_cast<const u32x4*>(region + row * RS + cb * 64);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x4 v = src[w];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b.v[4 * w + e] = __uint_as_float(v[e]);
+      }
+      if (grow < M && gcol < N)
+        enc::encode_block<kMode>(b, P, qo.q + (int64_t)grow * qld + gcol / 2,
+                                 qo.s + (int64_t)grow * sld + gcol / 16);
+    }
+  }
+}
+
 // Stage variants of the main loop (4-deep ring):
 //   kFull  - mid-stage sync waits for stage s+1 with one younger stage in
 //            flight, then refills the ring with stage s+3;
@@ -245,7 +296,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
     int M, int N, int K, const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
     const float* __restrict__ a_g, const uint8_t* __restrict__ b_q,
     const uint8_t* __restrict__ b_s, const float* __restrict__ b_g, void* __restrict__ y,
-    int y_dtype, int64_t ld_y, uint32_t y_bytes, int y_flags) {
+    int y_dtype, int64_t ld_y, uint32_t y_bytes, int y_flags, QuantOut qo) {
   static_assert(kStages == 4, "stage modes assume a 4-deep ring");
   using C = Cfg<BM, BN, WAVES_M, WAVES_N>;
   using L = Smem<BM, BN>;
@@ -455,15 +506,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   static_assert(C::kWaves * kRegion <= kStages * L::kBytes, "epilogue staging exceeds the ring");
   workgroup_barrier();
   uint8_t* region = smem + wave * kRegion;
-  if (y_dtype == 0)
+  if (y_dtype == 2) {
+    static_assert((C::FM >= 2 ? C::FM / 2 : 1) * 32 * (C::TN * 4 + 16) <= kRegion,
+                  "quantising epilogue staging exceeds the wave's region");
+    const float g = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(qo.g[0])));
+    const enc::EncodeParams P = enc::make_params(g);
+    const int mode = enc::encode_mode(g);
+    if (mode == 1) quant_tile<1>(acc, alpha, M, N, row0, col0, lane, region, qo, P);
+    else if (mode == 0) quant_tile<0>(acc, alpha, M, N, row0, col0, lane, region, qo, P);
+    else quant_tile<2>(acc, alpha, M, N, row0, col0, lane, region, qo, P);
+  } else if (y_dtype == 0) {
     store_tile<0>(acc, alpha, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
-  else
+  } else {
     store_tile<1>(acc, alpha, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
+  }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
-                      void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
+                      void* y, int y_dtype, int64_t ld_y, hipStream_t stream, QuantOut qo) {
   using L = Smem<BM, BN>;
   using C = Cfg<BM, BN, WAVES_M, WAVES_N>;
   const int smem = kStages * L::kBytes;
@@ -476,30 +537,30 @@ hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOp
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   // extent of y in bytes when below 4 GiB (whole tiles then use 32-bit
   // buffer offsets), else 0 (every tile takes the checked writer)
-  const int64_t extent = ((M - 1) * ld_y + N) * (y_dtype == 0 ? 4 : 2);
+  const int64_t extent = y_dtype == 2 ? 0 : ((M - 1) * ld_y + N) * (y_dtype == 0 ? 4 : 2);
   const uint32_t y_bytes = extent < (int64_t)0xFFFFFFFF ? (uint32_t)extent : 0u;
   // bit 0: rows start on 16-byte boundaries (16-byte stores of bf16 rows)
   const int y_flags = ((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ld_y % 8 == 0) ? 1 : 0;
   kern<<<(unsigned)tiles, C::kThreads, smem, stream>>>((int)M, (int)N, (int)K, a.q, a.s, a.g,
                                                         b.q, b.s, b.g, y, y_dtype, ld_y, y_bytes,
-                                                        y_flags);
+                                                        y_flags, qo);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
-                            void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
+                            void* y, int y_dtype, int64_t ld_y, hipStream_t stream, QuantOut qo) {
   // The largest tile that still fills the chip for at least one round (the
   // larger the tile, the fewer dequantisations per MFMA): 256 x 256, then
   // 256 x 128, else 128 x 128 (4x the workgroups of 256 x 256; two fit per
   // CU).
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (M >= 256 && N >= 256 && tiles(256, 256) >= 256)
-    return launch_cfg<256, 256, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream);
+    return launch_cfg<256, 256, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
   if (M >= 256 && N >= 128 && tiles(256, 128) >= 256)
-    return launch_cfg<256, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream);
-  return launch_cfg<128, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream);
+    return launch_cfg<256, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
+  return launch_cfg<128, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
 }
 
 }  // namespace nvfp4

@@ -26,6 +26,7 @@
 //  * The 8 per-wave partial tiles are summed through LDS in a fixed order, so
 //    results are deterministic (no atomics, no split-K across workgroups).
 #include "nvfp4_device.h"
+#include "nvfp4_encode.h"
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
@@ -127,8 +128,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(
     int N, int K, int M, const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
     const float* __restrict__ a_g, const uint8_t* __restrict__ b_q,
     const uint8_t* __restrict__ b_s, const float* __restrict__ b_g, void* __restrict__ y,
-    int y_dtype, int64_t ld_y) {
+    int y_dtype, int64_t ld_y, QuantOut qo) {
   __shared__ float red[kWaves][kRowsPerWG][32 + 1];
+  __shared__ float yt[32][kRowsPerWG + 4];  // NVFP4 output: 32 tokens x 32 columns
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,7 +183,29 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) s += red[v][wr][o >> 5];
       const int n = n0 + wr;
-      if (tok < M && n < N) store_out(y, (int64_t)tok * ld_y + n, s * alpha, y_dtype);
+      if (y_dtype == 2) yt[o >> 5][wr] = s * alpha;
+      else if (tok < M && n < N) store_out(y, (int64_t)tok * ld_y + n, s * alpha, y_dtype);
+    }
+    if (y_dtype == 2) {  // uniform
+      // the same fp32 values, quantised: lane t of the first wave encodes
+      // token t/2's block t%2 (16 columns) with the given global scale
+      __syncthreads();
+      if (tid < 64) {
+        const int tok = 32 * half + (tid >> 1), c0 = n0 + 16 * (tid & 1);
+        const float g = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(qo.g[0])));
+        const enc::EncodeParams P = enc::make_params(g);
+        const int mode = enc::encode_mode(g);
+        enc::Block16 b;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) b.v[e] = yt[tid >> 1][16 * (tid & 1) + e];
+        if (tok < M && c0 < N) {
+          uint8_t* qp = qo.q + (int64_t)tok * (N / 2) + c0 / 2;
+          uint8_t* sp = qo.s + (int64_t)tok * (N / 16) + c0 / 16;
+          if (mode == 1) enc::encode_block<1>(b, P, qp, sp);
+          else if (mode == 0) enc::encode_block<0>(b, P, qp, sp);
+          else enc::encode_block<2>(b, P, qp, sp);
+        }
+      }
     }
     __syncthreads();
   }
@@ -190,16 +214,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(
 }  // namespace
 
 hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
-                              void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
+                              void* y, int y_dtype, int64_t ld_y, hipStream_t stream, QuantOut qo) {
   const int64_t tiles = (N + kRowsPerWG - 1) / kRowsPerWG;
   // up to 64 tokens per launch; more rows go in 64-row passes over W (the
   // later passes find W in the Infinity Cache when it fits there)
   const size_t ysize = y_dtype == 0 ? 4 : 2;
   for (int64_t r0 = 0; r0 < M; r0 += 64) {
     const int64_t m = M - r0 < 64 ? M - r0 : 64;
+    QuantOut qp = qo;
+    if (y_dtype == 2) {
+      qp.q += r0 * (N / 2);
+      qp.s += r0 * (N / 16);
+    }
     gemm_decode_kernel<<<(unsigned)tiles, kThreads, 0, stream>>>(
         (int)N, (int)K, (int)m, a.q + r0 * (K / 2), a.s + r0 * (K / 16), a.g, b.q, b.s, b.g,
-        static_cast<uint8_t*>(y) + r0 * ld_y * (int64_t)ysize, y_dtype, ld_y);
+        y_dtype == 2 ? y : static_cast<uint8_t*>(y) + r0 * ld_y * (int64_t)ysize, y_dtype, ld_y, qp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -21,10 +21,20 @@ struct PackedOperand {
   const float* g;    // device scalar (or [G] for grouped weights)
 };
 
+// NVFP4 output of a dense GEMM (y_dtype 2): y quantised with the given
+// global scale *g (device fp32) into q [M, N/2] and s [M, N/16] (row-major,
+// contiguous, N % 16 == 0, q 8-byte aligned), from the same fp32 values
+// y_dtype 0 would store.
+struct QuantOut {
+  uint8_t* q;
+  uint8_t* s;
+  const float* g;
+};
+
 // gemm_generic.hip: any M, N, K % 16 == 0.
 hipError_t launch_gemm_generic(int64_t M, int64_t N, int64_t K, PackedOperand a,
                                PackedOperand b, void* y, int y_dtype, int64_t ld_y,
-                               hipStream_t stream);
+                               hipStream_t stream, QuantOut qo = {});
 
 // row_index (nullptr: none): grouped row r reads activation row row_index[r]
 // of the a_rows rows of `a`; an index outside [0, a_rows) reads as zeros.
@@ -36,12 +46,12 @@ hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets,
 // gemm_mfma.hip: K % 128 == 0, 16-byte aligned operand rows.
 hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a,
                             PackedOperand b, void* y, int y_dtype, int64_t ld_y,
-                            hipStream_t stream);
+                            hipStream_t stream, QuantOut qo = {});
 
 // gemm_skinny.hip: M <= 128 (decode; 64-row passes), K % 256 == 0, N * K / 2 < 4 GiB.
 hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a,
                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,
-                              hipStream_t stream);
+                              hipStream_t stream, QuantOut qo = {});
 
 // gemm_grouped.hip: K % 512 == 0, operands < 4 GiB; row_index as above.
 hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,

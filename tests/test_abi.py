@@ -168,3 +168,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         L.load()
+
+
+def _gq(**kw):
+    args = dict(M=8, N=32, K=128, a_q=P16, a_s=P16, a_g=P16, b_q=P16, b_s=P16, b_g=P16,
+                y_q=P16, y_s=P16, y_g=P16)
+    args.update(kw)
+    order = ("M", "N", "K", "a_q", "a_s", "a_g", "b_q", "b_s", "b_g", "y_q", "y_s", "y_g")
+    return nv.load().nvfp4_gemm_nvfp4_out(*[args[k] for k in order], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=40), nv.NVFP4_ERR_INVALID_ARG),          # blocks of 16 output columns
+    (dict(K=40), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(M=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y_g=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y_q=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y_s=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(b_s=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y_q=P4), nv.NVFP4_ERR_UNSUPPORTED),        # q rows are written 8 bytes at a time
+    (dict(M=1 << 31), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(M=0, y_q=NULL, y_s=NULL), nv.NVFP4_OK),
+    (dict(N=0), nv.NVFP4_OK),
+])
+def test_gemm_nvfp4_out_argument_checks(kw, status):
+    assert _gq(**kw) == status
