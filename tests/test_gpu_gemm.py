@@ -277,3 +277,21 @@ def test_strided_output_writers(out, pad, shift):
     idx = shift + (np.arange(M)[:, None] * ld + np.arange(N)[None, :])
     mask[idx.ravel()] = False
     assert np.all(full[mask] == -7.0), "writes outside the output view"
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 512, 512), (300, 384, 1024), (4096, 256, 128), (37, 48, 48)])
+@pytest.mark.parametrize("ga,gb", [(1e-30, 1e-12), (1e-30, 1e-15), (3e18, 3e18)])
+def test_bf16_output_rne_at_the_extremes(M, N, K, ga, gb):
+    """Global scales whose product is subnormal (outputs near or below the
+    smallest normal fp32) or huge (outputs overflow to infinity): the bf16
+    output still equals round-to-nearest-even of the fp32 output, on the
+    decode, MFMA (whole and edge tiles) and general kernels."""
+    need_gpu()
+    rng = np.random.default_rng(M + N)
+    a = to_gpu(*_rand_packed(rng, M, K, 0x30, 0x48), np.float32(ga))
+    b = to_gpu(*_rand_packed(rng, N, K, 0x30, 0x48), np.float32(gb))
+    note(f"bf16 extremes M={M} N={N} K={K} ga={ga} gb={gb}")
+    y32 = _gemm(a, b, "f32")
+    y16 = _gemm(a, b, "bf16")
+    ref = y32.cpu().to(torch.bfloat16)
+    assert torch.equal(ref.view(torch.int16), y16.cpu().view(torch.int16))
