@@ -320,21 +320,29 @@ def main():
         else:
             a = nv.nvfp4_quantize(wl.randn((total, k_), wl.seed_for(3, 2), "bf16").to(dev))
         ym = torch.empty((total, n_), dtype=torch.bfloat16, device=dev)
-        runs = [(proj, a, None)]
+        runs = [(proj, a, None, off, total)]
         if proj == "gate_up":
             # the same GEMM reading the token rows through the routing index
-            runs.append(("gate_up_gather", xq, rt.to(torch.int32)))
-        for name, a_op, ri in runs:
+            runs.append(("gate_up_gather", xq, rt.to(torch.int32), off, total))
+            # and under a skewed router: 110 experts in use, up to 488 rows each
+            sk = wl.moe_routing(wl.seed_for(3, 0), skew=1.0)
+            runs.append(("gate_up_skewed", xq, sk.row_token.to(torch.int32).to(dev),
+                         sk.m_offsets.to(dev), int(sk.m_offsets[-1])))
+            moe["skewed_router"] = {"skew": 1.0, "experts_used": int((sk.counts > 0).sum()),
+                                    "rows_per_expert_max": int(sk.counts.max())}
+        for name, a_op, ri, off_, tot_ in runs:
             # ~20-30 ms of untimed launches first: clocks settle under a new load
-            timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a_op, (bq, bs, bg), "bf16", y=ym,
+            timed(lambda i: nv.nvfp4_grouped_gemm(off_, tot_, a_op, (bq, bs, bg), "bf16", y=ym,
                                                   row_index=ri), 40)
-            ms = timed(lambda i: nv.nvfp4_grouped_gemm(off, total, a_op, (bq, bs, bg), "bf16",
+            ms = timed(lambda i: nv.nvfp4_grouped_gemm(off_, tot_, a_op, (bq, bs, bg), "bf16",
                                                        y=ym, row_index=ri), 20)
-            nbytes = E * n_ * k_ * 9 // 16 + total * k_ * 9 // 16 + total * n_ * 2
+            # weights of the experts that have rows (each read once), their rows, y
+            used = int((torch.diff(off_.cpu().to(torch.int64)) > 0).sum())
+            nbytes = used * n_ * k_ * 9 // 16 + tot_ * k_ * 9 // 16 + tot_ * n_ * 2
             gbs = nbytes / (ms * 1e-3) / 1e9
             moe[name] = {"N": n_, "K": k_, "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
                          "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "tflops": round(2.0 * total * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
+                         "tflops": round(2.0 * tot_ * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
         del bq, bs, bg, a, ym
 
     # Large outlier workload M = N = K = 16384 (1 % of entries x50): the

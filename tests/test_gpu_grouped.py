@@ -231,3 +231,32 @@ def test_strided_output(out, pad, shift):
     mask = np.ones(full.shape, bool)
     mask[(shift + np.arange(total)[:, None] * ld + np.arange(N)[None, :]).ravel()] = False
     assert np.all(full[mask] == -7.0), "writes outside the output view"
+
+
+@pytest.mark.parametrize("K,N", [(1024, 192), (768, 72)])
+def test_skewed_routing(K, N):
+    """Skewed router (a few experts take most tokens, most take none):
+    experts with hundreds of rows run many 32-token chunks, the others are
+    skipped; tokens are read through the routing index."""
+    need_gpu()
+    r = wl.moe_routing(wl.seed_for(3, 5), tokens=512, experts=64, topk=8, skew=2.0)
+    counts = torch.diff(r.m_offsets.to(torch.int64))
+    assert int(counts.max()) > 200 and int((counts == 0).sum()) > 10
+    rng = np.random.default_rng(K + N)
+    G, total = 64, int(r.m_offsets[-1])
+    aq, as_ = _rand_packed(rng, (512,), K)
+    ag = np.float32(0.05)
+    bq, bs = _rand_packed(rng, (G, N), K)
+    bg = (rng.random(G) + 0.5).astype(np.float32)
+    rt = r.row_token.numpy().astype(np.int64)
+    y_ref, bound = grouped_gemm_ref(r.m_offsets.numpy(), aq[rt], as_[rt], ag, bq, bs, bg)
+    dev = "cuda"
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)  # noqa: E731
+    note(f"grouped skewed routing K={K} N={N} max_rows={int(counts.max())}")
+    y = nv.nvfp4_grouped_gemm(r.m_offsets.to(dev), total,
+                              (t(aq), t(as_), torch.tensor([ag], device=dev)),
+                              (t(bq), t(bs), t(bg)), out_dtype="bf16",
+                              row_index=r.row_token.to(torch.int32).to(dev))
+    torch.cuda.synchronize()
+    ok, worst = check_gemm(np_(y), y_ref, bound, "bf16")
+    assert ok, worst

@@ -108,10 +108,16 @@ class MoeRouting:
 
 
 def moe_routing(seed: int, tokens: int = MOE_TOKENS, experts: int = MOE_EXPERTS,
-                topk: int = MOE_TOPK) -> MoeRouting:
+                topk: int = MOE_TOPK, skew: float = 0.0) -> MoeRouting:
     """Seeded softmax router over N(0,1) logits, top-k, rows sorted stably by
-    (expert, token).  Routing is harness bookkeeping, not part of the GEMM."""
+    (expert, token).  Routing is harness bookkeeping, not part of the GEMM.
+    ``skew`` > 0 lowers expert e's logit by skew * log(1 + e), so a few
+    experts draw most tokens and many draw none (the uneven routing the pages
+    caution about); skew 1.0 at 512 tokens x top-8 of 256 leaves 110 experts
+    in use, the busiest with 488 rows."""
     logits = randn((tokens, experts), seed, "fp32")
+    if skew:
+        logits = logits - skew * torch.log1p(torch.arange(experts, dtype=torch.float32))
     probs = torch.softmax(logits, dim=-1)
     expert_of = torch.topk(probs, topk, dim=-1).indices            # [T, k]
     token_of = torch.arange(tokens).unsqueeze(1).expand(-1, topk)  # [T, k]
