@@ -264,21 +264,32 @@ __device__ __forceinline__ void quant_tile(const f32x16 (&acc)[FM][FN], float al
         }
     // LDS accesses of one wave complete in order: the reads below see the
     // writes above, and the next pass's writes follow these reads
+    // blocks in groups of up to four: all of a group's LDS reads go out
+    // before its first encode, so the four encodes overlap each other's
+    // latency instead of each waiting on its own reads
+    constexpr int NT = NB / 64, GB = NT < 4 ? NT : 4;
 #pragma unroll
-    for (int t = 0; t < NB / 64; ++t) {
-      const int blk = t * 64 + lane, row = blk / BPR, cb = blk % BPR;
-      const int grow = row0 + pass * PR + row, gcol = col0 + cb * 16;
-      enc::Block16 b;
-      const u32x4* src = reinterpret_cast<const u32x4*>(region + row * RS + cb * 64);
+    for (int t0 = 0; t0 < NT; t0 += GB) {
+      enc::Block16 b[GB];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x4 v = src[w];
+      for (int u = 0; u < GB; ++u) {
+        const int blk = (t0 + u) * 64 + lane, row = blk / BPR, cb = blk % BPR;
+        const u32x4* src = reinterpret_cast<const u32x4*>(region + row * RS + cb * 64);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b.v[4 * w + e] = __uint_as_float(v[e]);
+        for (int w = 0; w < 4; ++w) {
+          const u32x4 v = src[w];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[u].v[4 * w + e] = __uint_as_float(v[e]);
+        }
       }
-      if (grow < M && gcol < N)
-        enc::encode_block<kMode>(b, P, qo.q + (int64_t)grow * qld + gcol / 2,
-                                 qo.s + (int64_t)grow * sld + gcol / 16);
+#pragma unroll
+      for (int u = 0; u < GB; ++u) {
+        const int blk = (t0 + u) * 64 + lane, row = blk / BPR, cb = blk % BPR;
+        const int grow = row0 + pass * PR + row, gcol = col0 + cb * 16;
+        if (grow < M && gcol < N)
+          enc::encode_block<kMode>(b[u], P, qo.q + (int64_t)grow * qld + gcol / 2,
+                                   qo.s + (int64_t)grow * sld + gcol / 16);
+      }
     }
   }
 }
