@@ -112,8 +112,9 @@ def moe_routing(seed: int, tokens: int = MOE_TOKENS, experts: int = MOE_EXPERTS,
     """Seeded softmax router over N(0,1) logits, top-k, rows sorted stably by
     (expert, token).  Routing is harness bookkeeping, not part of the GEMM.
     ``skew`` > 0 lowers expert e's logit by skew * log(1 + e), so a few
-    experts draw most tokens and many draw none (the uneven routing the pages
-    caution about); skew 1.0 at 512 tokens x top-8 of 256 leaves 110 experts
+    experts draw most tokens and many draw none (the uneven routing expected
+    in practice: "The Moment of Synthesis", "Assumptions and Potential
+    Mistakes"); skew 1.0 at 512 tokens x top-8 of 256 leaves 110 experts
     in use, the busiest with 488 rows."""
     logits = randn((tokens, experts), seed, "fp32")
     if skew:
