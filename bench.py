@@ -345,6 +345,28 @@ def main():
                          "tflops": round(2.0 * tot_ * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
         del bq, bs, bg, a, ym
 
+    # Same-box reference for the dense GEMM: the sustained rate of pure fp16
+    # MFMAs on every CU (the probe of --mode mfma_rate, no memory traffic,
+    # clock settled), and the GEMM's fraction of it.  Context only: the
+    # roofline above keeps the data-sheet peak.
+    probe_ref = None
+    try:
+        import ctypes
+        probe = ctypes.CDLL(os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_probe.so"))
+        probe.probe_mfma_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        pout = torch.empty(n_cu * 256, dtype=torch.float32, device=dev)
+        iters = 100000
+        launch = lambda i: probe.probe_mfma_rate(0, n_cu, 256, iters, pout.data_ptr(),  # noqa: E731
+                                                 ctypes.c_void_p(stream.cuda_stream))
+        timed(launch, 6)
+        pms = sorted(timed(launch, 1) for _ in range(3))[1]
+        ptf = n_cu * 4 * 4 * iters * 32768 / (pms * 1e-3) / 1e12
+        probe_ref = {"pure_fp16_mfma_tflops_all_cus": round(ptf, 1),
+                     "gemm_frac_of_it": round(gemm_tflops / ptf, 4)}
+    except OSError:
+        pass
+
     # Large outlier workload M = N = K = 16384 (1 % of entries x50): the
     # quantiser on x timed alone (two reads of x + the packed writes), then
     # the GEMM.  Inputs are drawn on the GPU (same recipe, CUDA generator).
@@ -397,6 +419,7 @@ def main():
         "moe_grouped": dict(moe, peak_GBps=PEAK_HBM_GBS),
         "large": large,
         "fused_quant_out": fused,
+        "mfma_sustained_probe": probe_ref,
         "mid_m": dict(mid_m, workload="m{64..1024}_n8192_k8192, 16 rotating weight copies"),
     }
     if not args.no_cpu_baseline:
