@@ -1,0 +1,97 @@
+"""The boundary's stream contract on the GPU: every entry point enqueues on
+the stream it is given (a side stream here, never the null stream), and a
+step of the path (quantise -> GEMM -> NVFP4-output GEMM -> grouped GEMM
+through the routing index) can be captured into a HIP graph and replayed:
+the library allocates nothing and issues no memset.  Every replay, with
+eager work and synchronisations between replays, must reproduce the eager
+results bit for bit (all kernels are deterministic)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_gemm_amd as nv
+import workloads as wl
+from tests.gpu_util import need_gpu, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(seed=5):
+    dev = "cuda"
+    x = wl.randn((512, 1024), seed, "bf16").to(dev)
+    w = wl.randn((768, 1024), seed + 1, "bf16").to(dev)
+    wq = nv.nvfp4_quantize(w)
+    counts = [40, 0, 70, 18, 100]
+    off = wl.ragged_offsets(counts).to(dev)
+    total = sum(counts)
+    bq = torch.stack([wq[0][:256]] * len(counts)).contiguous()
+    bs = torch.stack([wq[1][:256]] * len(counts)).contiguous()
+    bg = wq[2].repeat(len(counts))
+    idx = torch.from_numpy(np.random.default_rng(seed).integers(0, 512, total).astype(np.int32)).to(dev)
+    bufs = dict(
+        xq=(torch.empty((512, 512), dtype=torch.uint8, device=dev),
+            torch.empty((512, 64), dtype=torch.uint8, device=dev),
+            torch.empty(1, device=dev)),
+        ws=torch.empty(max(nv.nvfp4_quantize_workspace_bytes(512, 1024), 4), dtype=torch.uint8,
+                       device=dev),
+        y=torch.empty((512, 768), dtype=torch.bfloat16, device=dev),
+        yq=(torch.empty((512, 384), dtype=torch.uint8, device=dev),
+            torch.empty((512, 48), dtype=torch.uint8, device=dev)),
+        yg=torch.tensor([0.01], device=dev),
+        yt=torch.empty((total, 256), dtype=torch.float32, device=dev))
+    return x, wq, (off, total, (bq, bs, bg), idx), bufs
+
+
+def _step(x, wq, grouped, b, stream=None):
+    off, total, bw, idx = grouped
+    nv.nvfp4_quantize(x, out=b["xq"], workspace=b["ws"], stream=stream)
+    nv.nvfp4_gemm(b["xq"], wq, "bf16", y=b["y"], stream=stream)
+    nv.nvfp4_gemm_nvfp4_out(b["xq"], wq, b["yg"], out=b["yq"], stream=stream)
+    nv.nvfp4_grouped_gemm(off, total, b["xq"], bw, "f32", y=b["yt"], stream=stream,
+                          row_index=idx)
+
+
+def _snapshot(b):
+    return [t.clone() for t in (*b["xq"], b["y"], *b["yq"], b["yt"])]
+
+
+def test_side_stream():
+    need_gpu()
+    x, wq, grouped, b = _setup()
+    _step(x, wq, grouped, b)
+    torch.cuda.synchronize()
+    ref = _snapshot(b)
+    for t in (*b["xq"], b["y"], *b["yq"], b["yt"]):
+        t.zero_()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    note("entry points on a side stream")
+    with torch.cuda.stream(side):
+        _step(x, wq, grouped, b, stream=side)
+    side.synchronize()
+    for r, g in zip(ref, _snapshot(b)):
+        assert torch.equal(r, g)
+
+
+def test_graph_capture_and_replay():
+    need_gpu()
+    x, wq, grouped, b = _setup(seed=9)
+    _step(x, wq, grouped, b)          # eager (also warms up the launchers)
+    torch.cuda.synchronize()
+    ref = _snapshot(b)
+    g = torch.cuda.CUDAGraph()
+    for t in (*b["xq"], b["y"], *b["yq"], b["yt"]):
+        t.zero_()
+    torch.cuda.synchronize()
+    note("capture the step into a graph")
+    with torch.cuda.graph(g):
+        _step(x, wq, grouped, b)
+    for rep in range(3):
+        for t in (*b["xq"], b["y"], *b["yq"], b["yt"]):
+            t.fill_(3)                # eager work between replays
+        torch.cuda.synchronize()
+        note(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for r, got in zip(ref, _snapshot(b)):
+            assert torch.equal(r, got), f"replay {rep} differs"
