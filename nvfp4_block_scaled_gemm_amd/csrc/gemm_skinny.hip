@@ -9,16 +9,25 @@
 // dequantise-and-multiply work under that stream:
 //
 //  * One workgroup owns 32 weight rows (an n-tile) over all of K.  Its 8 waves
-//    split K in units of 256 elements; in a unit, lane group q of a wave holds
-//    the 64 contiguous elements [64q, 64q+64) of its row: 32 nibble bytes
-//    (two 16-byte loads) and 4 scale bytes, so four lanes cover a row's
-//    128-byte line.
-//  * Every load of a wave (up to 4 units of weights and activations) is
-//    issued before the first product, unit by unit.  All loads are
-//    unconditional buffer loads (rows past the operands read as zero), so
-//    the compiler's wait before unit i's products leaves the later units'
-//    loads in flight and the products overlap the weight stream (loads
-//    under a branch would make it wait for all of them).
+//    split K in units of 256 elements; for the products, lane group q of a
+//    wave holds the 64 contiguous elements [64q, 64q+64) of its row: 32
+//    nibble bytes and 4 scale bytes.
+//  * Every workgroup reads all of x, so at M = 32 a CU pulls as many
+//    activation bytes (from L2) as weight bytes (from HBM).  Measured on the
+//    MI355X, a CU's loads are limited by the cache lines it has in flight:
+//    loads that cover half lines (4 lanes x 16 bytes of 16 rows) make each
+//    activation byte cost about as much as a weight byte.  Activation
+//    nibbles are therefore loaded by whole 128-byte lines (lane L: row L % 8
+//    of the fragment's first or second eight rows, 16 bytes at 16 * (L / 8))
+//    and moved into the product layout by two DPP row rotations per dword
+//    pair.  Weights keep the direct layout (each lane loads its own 32
+//    bytes), which needs no merge: the same whole-line scheme for them saves
+//    load time but its merges cost more than that.
+//  * Loads are software-pipelined one unit deep and ordered by first use
+//    (activations, weight scales, then the first and the second 16 bytes of
+//    each weight fragment), so a unit's products wait on the weight stream
+//    piece by piece.  Deeper pipelines (more units in flight per wave) were
+//    measured slower at every M.
 //  * Products run on v_mfma_f32_16x16x32_f16 with weights as the 16-row A
 //    operand and up to 64 tokens as one to four B operands; both sides are
 //    dequantised exactly to fp16 in registers.  K is permuted identically on
@@ -41,6 +50,10 @@ constexpr int kUnitK = 256;      // K elements per wave step
 template <int NX>
 constexpr int max_units() { return NX > 2 ? 2 : 4; }
 constexpr uint32_t kOob = 0xFFFFFFF0u;  // offset past every operand (reads zero)
+#ifndef NVFP4_DECODE_DEPTH
+#define NVFP4_DECODE_DEPTH 1
+#endif
+constexpr int kDepth = NVFP4_DECODE_DEPTH;  // units in flight per wave
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -58,22 +71,60 @@ struct Unit {
   uint32_t s;  // 4 scale bytes
 };
 
-// Loads a unit at byte offsets qo (nibbles) and so (scales); offsets past
-// the range read as zero.
+// Byte offsets of one operand's 16-row fragment for this lane.
+struct Frag {
+  uint32_t q0, q1;  // the two 16-byte nibble loads of unit 0 (kOob past the rows)
+  uint32_t s;       // the lane's 4 scale bytes of unit 0 (kOob past the rows)
+};
+
+// Fragment rows r0 .. r0+15 of an operand with `rows` rows.  Whole lines:
+// nibble load h (0, 1) gives lane L the 16 bytes at 16 * (L / 8) of row
+// r0 + 8h + L % 8 (merge_unit then sorts them).  Direct: lane (li, lq) =
+// (L % 16, L / 16) loads bytes 32lq .. 32lq+31 of row r0 + li.  Either way
+// the scale load gives lane (li, lq) bytes 4lq .. 4lq+3 of row r0 + li's
+// unit scales.
+template <bool kWhole>
+__device__ __forceinline__ Frag make_frag(int r0, int rows, uint32_t qrow, uint32_t srow, int lane) {
+  const int rs = r0 + (lane & 15);
+  const uint32_t so = rs < rows ? (uint32_t)rs * srow + (uint32_t)(lane >> 4) * 4u : kOob;
+  if constexpr (kWhole) {
+    const int ra = r0 + (lane & 7), rb = ra + 8;
+    const uint32_t col = (uint32_t)(lane >> 3) * 16u;
+    return Frag{ra < rows ? (uint32_t)ra * qrow + col : kOob, rb < rows ? (uint32_t)rb * qrow + col : kOob, so};
+  } else {
+    // half lines: lane (li, lq) loads its own 32 bytes, no merge needed
+    const uint32_t o = (uint32_t)rs * qrow + (uint32_t)(lane >> 4) * 32u;
+    return Frag{rs < rows ? o : kOob, rs < rows ? o + 16u : kOob, so};
+  }
+}
+
+// Loads a unit whose bytes sit uq (nibbles) and us (scales) past unit 0;
+// offsets past the range read as zero.  The two whole-line nibble loads a, b
+// are merged into the product layout: lane l (row l % 16) needs the chunks
+// 2(l/16) and 2(l/16)+1 of its row, which lanes l and l ^ 8 hold between
+// them (l % 16 < 8: a[l], a[l ^ 8]; else b[l ^ 8], b[l]).
 __device__ __forceinline__ Unit load_unit(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
-                                          uint32_t qo, uint32_t so, bool ok) {
+                                          const Frag& f, uint32_t uq, uint32_t us, bool in) {
+  const u32x4 a = ld16(rq, in && f.q0 != kOob ? f.q0 + uq : kOob);
+  const u32x4 b = ld16(rq, in && f.q1 != kOob ? f.q1 + uq : kOob);
   Unit r;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) r.q[i] = ld16(rq, ok ? qo + 16u * i : kOob);
-  r.s = ld4(rs, ok ? so : kOob);
+  r.s = ld4(rs, in && f.s != kOob ? f.s + us : kOob);
+  r.q[0] = a;  // merged after the loads arrive (see merge_unit)
+  r.q[1] = b;
   return r;
 }
 
-// Byte offsets of one operand's fragment row for this lane.
-struct Frag {
-  uint32_t q, s;  // offsets of the lane's part of unit 0
-  bool ok;        // the row exists
-};
+// DPP row rotation by 8 lanes (lane l of each 16-lane row reads lane l ^ 8),
+// written only to the lanes of the bank mask; the others keep `old`.
+constexpr int kRowRor8 = 0x128;
+__device__ __forceinline__ void merge_unit(Unit& u) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int a = (int)u.q[0][d], b = (int)u.q[1][d];
+    u.q[0][d] = (uint32_t)__builtin_amdgcn_update_dpp(a, b, kRowRor8, 0xF, 0xC, false);
+    u.q[1][d] = (uint32_t)__builtin_amdgcn_update_dpp(b, a, kRowRor8, 0xF, 0x3, false);
+  }
+}
 
 // The tokens (<= 16 * NX) against the 32-row tile, over all of K; leaves the
 // wave's partial sums in acc[f][g] (weight fragment f, token fragment g).
@@ -89,19 +140,40 @@ __device__ __forceinline__ void chunk_partial(__amdgpu_buffer_rsrc_t wq, __amdgp
     for (int g = 0; g < 4; ++g) acc[f][g] = f32x4{0, 0, 0, 0};
   for (int ub = wave; ub < nunits; ub += kWaves * kMaxUnits) {
     Unit wu[kMaxUnits][2], xu[kMaxUnits][NX];
-#pragma unroll
-    for (int i = 0; i < kMaxUnits; ++i) {
+    auto load = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       const int u = ub + i * kWaves;
       const bool in = u < nunits;
       const uint32_t uq = (uint32_t)u * (kUnitK / 2), us = (uint32_t)u * (kUnitK / 16);
+      // Order of a unit's loads = order of first use: the activations (from
+      // L2; merged first), the weight scales, then the first 16 bytes of each
+      // weight fragment (MFMA steps 0-3) before the second (steps 4-7), so
+      // the products wait on the weight stream piece by piece.
 #pragma unroll
-      for (int f = 0; f < 2; ++f) wu[i][f] = load_unit(wq, ws, w[f].q + uq, w[f].s + us, in && w[f].ok);
+      for (int g = 0; g < NX; ++g) xu[i][g] = load_unit(xq, xs, x[g], uq, us, in);
 #pragma unroll
-      for (int g = 0; g < NX; ++g) xu[i][g] = load_unit(xq, xs, x[g].q + uq, x[g].s + us, in && x[g].ok);
-    }
+      for (int f = 0; f < 2; ++f) wu[i][f].s = ld4(ws, in && w[f].s != kOob ? w[f].s + us : kOob);
 #pragma unroll
-    for (int i = 0; i < kMaxUnits; ++i) {
-      if (ub + i * kWaves >= nunits) break;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const uint32_t o = h == 0 ? w[f].q0 : w[f].q1;
+          wu[i][f].q[h] = ld16(wq, in && o != kOob ? o + uq : kOob);
+        }
+    };
+    // Software pipeline, kDepth units in flight: the loads of unit
+    // i + kDepth - 1 go out before the products of unit i.  Every unit is
+    // multiplied, also those past K (their loads read zeros, which add exact
+    // zeros), so there is no branch for the compiler to sink loads into, and
+    // scheduling barriers keep each unit's loads at their place in the order.
+    constexpr int kD = kDepth < kMaxUnits ? kDepth : kMaxUnits;
+    static_for<kD>([&](auto ic) { load(ic); });
+    static_for<kMaxUnits>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i > 0 && i + kD - 1 < kMaxUnits) load(std::integral_constant<int, i + kD - 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < NX; ++g) merge_unit(xu[i][g]);
       Scales sw[2], sx[NX];
 #pragma unroll
       for (int f = 0; f < 2; ++f) sw[f] = to_scales(wu[i][f].s);
@@ -120,7 +192,7 @@ __device__ __forceinline__ void chunk_partial(__amdgpu_buffer_rsrc_t wq, __amdgp
         }
         __builtin_amdgcn_sched_barrier(0);  // keep each step's dequant beside its MFMAs
       });
-    }
+    });
   }
 }
 
@@ -143,18 +215,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(
   const int nunits = K / kUnitK;
   const float alpha = a_g[0] * b_g[0];
 
-  // weight rows of this lane: n0 + 16 f + li; token rows: 16 g + li
+  // weight rows of this lane's products: n0 + 16 f + li; token rows: 16 g + li
   Frag w[2], x[4];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const uint32_t row = (uint32_t)(n0 + 16 * f + li);
-    w[f] = Frag{row * qrow + (uint32_t)lq * 32u, row * srow + (uint32_t)lq * 4u, row < (uint32_t)N};
-  }
+  for (int f = 0; f < 2; ++f) w[f] = make_frag<false>(n0 + 16 * f, N, qrow, srow, lane);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const uint32_t tok = (uint32_t)(16 * g + li);
-    x[g] = Frag{tok * qrow + (uint32_t)lq * 32u, tok * srow + (uint32_t)lq * 4u, tok < (uint32_t)M};
-  }
+  for (int g = 0; g < 4; ++g) x[g] = make_frag<true>(16 * g, M, qrow, srow, lane);
 
   f32x4 acc[2][4];
   if (M > 32) chunk_partial<4>(wq, ws, xq, xs, w, x, nunits, wave, acc);  // uniform
