@@ -103,10 +103,13 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of x in the CPU oracle sample (4096 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy", "mfma_rate"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "copy", "mfma_rate", "stream_rate"],
+                    default="bench",
                     help="copy: a plain 1 GiB device copy, for HBM counter calibration; "
                          "mfma_rate: the sustained fp16 MFMA rate alone and with 4 or 8 "
-                         "dequantisation instructions per MFMA, on one CU and on all of them")
+                         "dequantisation instructions per MFMA, on one CU and on all of them; "
+                         "stream_rate: the grouped GEMM's weight-load pattern streaming "
+                         "gate_up-sized weights with nothing else running")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -162,6 +165,44 @@ def main():
                     "valu_per_mfma": nv_ops, "us": round(us, 1),
                     "ns_per_mfma_per_simd": round(ns_per_mfma, 3),
                     "tflops": round(busy_cus * 4 * 32768 / ns_per_mfma / 1e3, 1)}), flush=True)
+        return
+
+    if args.mode == "stream_rate":
+        import ctypes
+        probe = ctypes.CDLL(os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_probe.so"))
+        probe.probe_stream_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        stream = torch.cuda.current_stream()
+        n_items = 16384                                  # x 64 rows = 256 experts x 4096 rows
+        w = torch.full((n_items * 64 * 3072,), 0x11, dtype=torch.uint8, device=dev)
+        s = torch.full((n_items * 64 * 384,), 0x38, dtype=torch.uint8, device=dev)
+        out = torch.zeros(1, dtype=torch.int32, device=dev)
+        names = {0: "64 rows x 256 B jobs, nibbles only",
+                 1: "64 rows x 256 B jobs + scales 32 rows x 32 B per load (the grouped kernel)",
+                 2: "64 rows x 256 B jobs + scales by whole lines",
+                 3: "128 rows x 128 B jobs + scales 64 rows x 16 B per load"}
+        for mode, busy in ((0, 0), (1, 0), (2, 0), (3, 0), (1, 500), (1, 1000)):
+            ni = n_items // 2 if mode == 3 else n_items
+
+            def launch():
+                rc = probe.probe_stream_rate(mode, w.data_ptr(), s.data_ptr(), ni, busy, n_cu,
+                                             out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+                assert rc == 0, f"probe_stream_rate returned {rc}"
+            for _ in range(5):
+                launch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 10
+            nbytes = w.numel() + (s.numel() if mode else 0)
+            print(json.dumps({"mode": "stream_rate", "pattern": names[mode],
+                              "busy_fmas_per_job": busy, "us": round(us, 1), "bytes": nbytes,
+                              "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
         return
 
     cfg = wl.LINEAR
