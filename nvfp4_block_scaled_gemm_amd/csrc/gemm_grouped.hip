@@ -22,7 +22,10 @@
 //    brings 18 KB of packed weights (64 rows x 256 B of nibbles + 32 B of
 //    scales) into a private 2-slot LDS ring with 16-byte buffer-to-LDS loads,
 //    and the chunk's activations (64 B of nibbles + 8 B of scales per lane
-//    and token fragment) into registers.  Rows past the operands read as
+//    and token fragment) into registers.  A job issues its activation loads
+//    before its weight loads, so the wait for the job ends on the weight
+//    stream rather than on activations queued behind it (measured 1.5 %
+//    faster on every MoE shape).  Rows past the operands read as
 //    zero; token rows outside the expert's chunk are not fetched.  Loads run
 //    one job ahead and every job issues the same 28 memory instructions (a
 //    finished wave pads with harmless reloads), so one fixed s_waitcnt per
@@ -238,11 +241,6 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
     const uint32_t xs_job = (uint32_t)c.u * kRowSc + (uint32_t)lq * 8u;
     uint8_t* slot = ring + S * kSlotBytes;
 #pragma unroll
-    for (int k = 0; k < kNibLoads; ++k) dma16(wq, wq_bytes, wq_job + wq_lane[k], slot + k * 1024);
-#pragma unroll
-    for (int m = 0; m < kScLoads; ++m)
-      dma16(ws, ws_bytes, ws_job + 32u * m * srow + ws_lane, slot + kSlotNib + m * 1024);
-#pragma unroll
     for (int g = 0; g < 2; ++g) {
       // token rows outside the expert's chunk are not fetched at all
       const bool ok = live && c.xq[g] != kOob;
@@ -251,6 +249,11 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
       for (int i = 0; i < 4; ++i) xs[S].q[g][i] = ld16(a_q, xq_bytes, ok ? qo + 16u * i : kOob);
       xs[S].s[g] = ld8(a_s, xs_bytes, ok ? c.xs[g] + xs_job : kOob);
     }
+#pragma unroll
+    for (int k = 0; k < kNibLoads; ++k) dma16(wq, wq_bytes, wq_job + wq_lane[k], slot + k * 1024);
+#pragma unroll
+    for (int m = 0; m < kScLoads; ++m)
+      dma16(ws, ws_bytes, ws_job + 32u * m * srow + ws_lane, slot + kSlotNib + m * 1024);
   };
 
   f32x4 acc[kFrags][2];
