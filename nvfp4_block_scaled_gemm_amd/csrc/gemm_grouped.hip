@@ -25,7 +25,7 @@
 //    and token fragment) into registers.  A job issues its activation loads
 //    before its weight loads, so the wait for the job ends on the weight
 //    stream rather than on activations queued behind it (measured 1.5 %
-//    faster on every MoE shape).  Rows past the operands read as
+//    faster on the balanced MoE shapes).  Rows past the operands read as
 //    zero; token rows outside the expert's chunk are not fetched.  Loads run
 //    one job ahead and every job issues the same 28 memory instructions (a
 //    finished wave pads with harmless reloads), so one fixed s_waitcnt per
