@@ -5,8 +5,8 @@
 // 16-64 tokens reach a small fraction of the big-GEMM rate (magik.net "The
 // Moment of Recalibration", "Input Knowledge", previous benchmark results).
 // The kernel is therefore built to move the packed weights from HBM once, at
-// full line width, with as many bytes in flight as possible, and to hide the
-// dequantise-and-multiply work under that stream:
+// full line width, and to hide the dequantise-and-multiply work under that
+// stream:
 //
 //  * One workgroup owns 32 weight rows (an n-tile) over all of K.  Its 8 waves
 //    split K in units of 256 elements; for the products, lane group q of a
@@ -14,9 +14,9 @@
 //    nibble bytes and 4 scale bytes.
 //  * Every workgroup reads all of x, so at M = 32 a CU pulls as many
 //    activation bytes (from L2) as weight bytes (from HBM).  Measured on the
-//    MI355X, a CU's loads are limited by the cache lines it has in flight:
-//    loads that cover half lines (4 lanes x 16 bytes of 16 rows) make each
-//    activation byte cost about as much as a weight byte.  Activation
+//    MI355X, loads that cover half lines (4 lanes x 16 bytes of 16 rows)
+//    make each activation byte cost about as much as a weight byte, while
+//    loads of the same bytes by whole lines cost far less.  Activation
 //    nibbles are therefore loaded by whole 128-byte lines (lane L: row L % 8
 //    of the fragment's first or second eight rows, 16 bytes at 16 * (L / 8))
 //    and moved into the product layout by two DPP row rotations per dword
