@@ -20,9 +20,11 @@
 //    nibbles are therefore loaded by whole 128-byte lines (lane L: row L % 8
 //    of the fragment's first or second eight rows, 16 bytes at 16 * (L / 8))
 //    and moved into the product layout by two DPP row rotations per dword
-//    pair.  Weights keep the direct layout (each lane loads its own 32
-//    bytes), which needs no merge: the same whole-line scheme for them saves
-//    load time but its merges cost more than that.
+//    pair; so are the weights' (their loads get faster by a little more than
+//    the merges cost: M = 16 / 32 12.1 / 14.9 against 12.3 / 15.2 us).  Up
+//    to 8 tokens both keep the direct layout (each lane loads its own 32
+//    bytes, no merges): the activations are then few bytes, and whole-line
+//    weights alone measured slower there (M = 1 11.4 against 11.1 us).
 //  * Loads are software-pipelined one unit deep and ordered by first use
 //    (activations, weight scales, then the first and the second 16 bytes of
 //    each weight fragment), so a unit's products wait on the weight stream
@@ -99,8 +101,9 @@ __device__ __forceinline__ Frag make_frag(int r0, int rows, uint32_t qrow, uint3
 }
 
 // Loads a unit whose bytes sit uq (nibbles) and us (scales) past unit 0;
-// offsets past the range read as zero.  The two whole-line nibble loads a, b
-// are merged into the product layout: lane l (row l % 16) needs the chunks
+// offsets past the range read as zero.  Direct fragments: q[0], q[1] are the
+// lane's own 32 bytes.  Whole-line fragments: the two loads are merged into
+// the product layout later (merge_unit): lane l (row l % 16) needs chunks
 // 2(l/16) and 2(l/16)+1 of its row, which lanes l and l ^ 8 hold between
 // them (l % 16 < 8: a[l], a[l ^ 8]; else b[l ^ 8], b[l]).
 __device__ __forceinline__ Unit load_unit(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
@@ -128,7 +131,9 @@ __device__ __forceinline__ void merge_unit(Unit& u) {
 
 // The tokens (<= 16 * NX) against the 32-row tile, over all of K; leaves the
 // wave's partial sums in acc[f][g] (weight fragment f, token fragment g).
-template <int NX>
+// WL: both operands' fragments were made whole-line (make_frag<true>) and are
+// merged after they land; otherwise both are direct (make_frag<false>).
+template <int NX, bool WL>
 __device__ __forceinline__ void chunk_partial(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t ws,
                                               __amdgpu_buffer_rsrc_t xq, __amdgpu_buffer_rsrc_t xs,
                                               const Frag (&w)[2], const Frag (&x)[4], int nunits,
@@ -146,20 +151,32 @@ __device__ __forceinline__ void chunk_partial(__amdgpu_buffer_rsrc_t wq, __amdgp
       const bool in = u < nunits;
       const uint32_t uq = (uint32_t)u * (kUnitK / 2), us = (uint32_t)u * (kUnitK / 16);
       // Order of a unit's loads = order of first use: the activations (from
-      // L2; merged first), the weight scales, then the first 16 bytes of each
-      // weight fragment (MFMA steps 0-3) before the second (steps 4-7), so
-      // the products wait on the weight stream piece by piece.
+      // L2), the weight scales, then the weight nibbles.  Whole-line weight
+      // fragments go one after the other (fragment 0 is merged while 1
+      // lands); direct ones give the first 16 bytes of both fragments (MFMA
+      // steps 0-3) before the second (steps 4-7), so the products wait on the
+      // weight stream piece by piece.
 #pragma unroll
       for (int g = 0; g < NX; ++g) xu[i][g] = load_unit(xq, xs, x[g], uq, us, in);
 #pragma unroll
       for (int f = 0; f < 2; ++f) wu[i][f].s = ld4(ws, in && w[f].s != kOob ? w[f].s + us : kOob);
+      if constexpr (WL) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const uint32_t o = h == 0 ? w[f].q0 : w[f].q1;
-          wu[i][f].q[h] = ld16(wq, in && o != kOob ? o + uq : kOob);
-        }
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t o = h == 0 ? w[f].q0 : w[f].q1;
+            wu[i][f].q[h] = ld16(wq, in && o != kOob ? o + uq : kOob);
+          }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const uint32_t o = h == 0 ? w[f].q0 : w[f].q1;
+            wu[i][f].q[h] = ld16(wq, in && o != kOob ? o + uq : kOob);
+          }
+      }
     };
     // Software pipeline, kDepth units in flight: the loads of unit
     // i + kDepth - 1 go out before the products of unit i.  Every unit is
@@ -172,8 +189,12 @@ __device__ __forceinline__ void chunk_partial(__amdgpu_buffer_rsrc_t wq, __amdgp
       constexpr int i = decltype(ic)::value;
       if constexpr (i > 0 && i + kD - 1 < kMaxUnits) load(std::integral_constant<int, i + kD - 1>{});
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (WL) {
 #pragma unroll
-      for (int g = 0; g < NX; ++g) merge_unit(xu[i][g]);
+        for (int g = 0; g < NX; ++g) merge_unit(xu[i][g]);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) merge_unit(wu[i][f]);
+      }
       Scales sw[2], sx[NX];
 #pragma unroll
       for (int f = 0; f < 2; ++f) sw[f] = to_scales(wu[i][f].s);
@@ -215,17 +236,27 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(
   const int nunits = K / kUnitK;
   const float alpha = a_g[0] * b_g[0];
 
-  // weight rows of this lane's products: n0 + 16 f + li; token rows: 16 g + li
+  // weight rows of this lane's products: n0 + 16 f + li; token rows: 16 g + li.
+  // More than 8 tokens: whole-line loads of both operands; up to 8 the
+  // activations are few bytes and the direct layout needs no merges.
   Frag w[2], x[4];
+  if (M > 8) {  // uniform
 #pragma unroll
-  for (int f = 0; f < 2; ++f) w[f] = make_frag<false>(n0 + 16 * f, N, qrow, srow, lane);
+    for (int f = 0; f < 2; ++f) w[f] = make_frag<true>(n0 + 16 * f, N, qrow, srow, lane);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) x[g] = make_frag<true>(16 * g, M, qrow, srow, lane);
+    for (int g = 0; g < 4; ++g) x[g] = make_frag<true>(16 * g, M, qrow, srow, lane);
+  } else {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) w[f] = make_frag<false>(n0 + 16 * f, N, qrow, srow, lane);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x[g] = make_frag<false>(16 * g, M, qrow, srow, lane);
+  }
 
   f32x4 acc[2][4];
-  if (M > 32) chunk_partial<4>(wq, ws, xq, xs, w, x, nunits, wave, acc);  // uniform
-  else if (M > 16) chunk_partial<2>(wq, ws, xq, xs, w, x, nunits, wave, acc);
-  else chunk_partial<1>(wq, ws, xq, xs, w, x, nunits, wave, acc);
+  if (M > 32) chunk_partial<4, true>(wq, ws, xq, xs, w, x, nunits, wave, acc);  // uniform
+  else if (M > 16) chunk_partial<2, true>(wq, ws, xq, xs, w, x, nunits, wave, acc);
+  else if (M > 8) chunk_partial<1, true>(wq, ws, xq, xs, w, x, nunits, wave, acc);
+  else chunk_partial<1, false>(wq, ws, xq, xs, w, x, nunits, wave, acc);
 
   // Partial tiles -> LDS and a fixed-order sum over the waves, 32 tokens at
   // a time: acc[f][g] reg r is weight row 16f + 4*lq + r, token 16g + li.
