@@ -141,11 +141,27 @@ struct Cfg {
   // direct-load instructions per wave per stage
   static constexpr int kANibLoads = BM * kRowBytes / 1024 / kWaves;
   static constexpr int kBNibLoads = BN * kRowBytes / 1024 / kWaves;
-  static constexpr int kAScLoads = BM * kScBytes / 256 / kWaves;
-  static constexpr int kBScLoads = BN * kScBytes / 256 / kWaves;
+  // scale loads (4 bytes per lane) of a whole stage; a tile with fewer
+  // than one per wave gives every wave one, the extra waves repeating one
+  // exactly (identical bytes to the same LDS slot), so that every wave
+  // issues the same number of loads and the fixed waits stay exact
+  static constexpr int kAScTotal = BM * kScBytes / 256;
+  static constexpr int kBScTotal = BN * kScBytes / 256;
+  static constexpr int kAScLoads = kAScTotal >= kWaves ? kAScTotal / kWaves : 1;
+  static constexpr int kBScLoads = kBScTotal >= kWaves ? kBScTotal / kWaves : 1;
   static constexpr int kLoads = kANibLoads + kBNibLoads + kAScLoads + kBScLoads;
-  static_assert(kANibLoads >= 1 && kBNibLoads >= 1 && kAScLoads >= 1 && kBScLoads >= 1,
+  static_assert(kANibLoads >= 1 && kBNibLoads >= 1 && kAScTotal >= 1 && kBScTotal >= 1,
                 "tile too small for the load split");
+  static_assert((kAScTotal < kWaves || kAScTotal % kWaves == 0) &&
+                    (kBScTotal < kWaves || kBScTotal % kWaves == 0),
+                "scale loads split evenly over the waves");
+  // first scale-load slot of wave w
+  static __device__ __forceinline__ int asc_slot(int w) {
+    return kAScTotal >= kWaves ? w * kAScLoads : w % kAScTotal;
+  }
+  static __device__ __forceinline__ int bsc_slot(int w) {
+    return kBScTotal >= kWaves ? w * kBScLoads : w % kBScTotal;
+  }
 };
 
 // Output tile writer.  acc[i][j] register r holds row 8*(r/4) + 4*(lane/32)
@@ -313,6 +329,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   using L = Smem<BM, BN>;
   constexpr int FM = C::FM, FN = C::FN, NF = FM + FN, Q = FM * FN;
   constexpr int P = 2 * NF;  // dequant pieces per MFMA step
+  static_assert(NF <= 2 * Q, "the lo reads of a stage fit in the MFMAs of steps 3 and 4");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -346,12 +363,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   }
 #pragma unroll
   for (int i = 0; i < C::kAScLoads; ++i) {
-    const int slot = (wave * C::kAScLoads + i) * 64 + lane;     // 4-byte LDS slot
+    const int slot = (C::asc_slot(wave) + i) * 64 + lane;        // 4-byte LDS slot
     a_sc_off[i] = (uint32_t)min(m0 + (slot >> 1), M - 1) * rows + ((slot & 1) << 2);
   }
 #pragma unroll
   for (int i = 0; i < C::kBScLoads; ++i) {
-    const int slot = (wave * C::kBScLoads + i) * 64 + lane;
+    const int slot = (C::bsc_slot(wave) + i) * 64 + lane;
     b_sc_off[i] = (uint32_t)min(n0 + (slot >> 1), N - 1) * rows + ((slot & 1) << 2);
   }
 
@@ -375,11 +392,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
                         b_nib_off[i], (uint32_t)st * kRowBytes);
     } else if constexpr (J < C::kANibLoads + C::kBNibLoads + C::kAScLoads) {
       constexpr int i = J - C::kANibLoads - C::kBNibLoads;
-      buffer_load_lds4(a_s, as_bytes, base + L::kASc + (wave * C::kAScLoads + i) * 256,
+      buffer_load_lds4(a_s, as_bytes, base + L::kASc + (C::asc_slot(wave) + i) * 256,
                        a_sc_off[i], (uint32_t)st * kScBytes);
     } else {
       constexpr int i = J - C::kANibLoads - C::kBNibLoads - C::kAScLoads;
-      buffer_load_lds4(b_s, bs_bytes, base + L::kBSc + (wave * C::kBScLoads + i) * 256,
+      buffer_load_lds4(b_s, bs_bytes, base + L::kBSc + (C::bsc_slot(wave) + i) * 256,
                        b_sc_off[i], (uint32_t)st * kScBytes);
     }
   };
@@ -462,11 +479,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
           }
         });
         if constexpr ((T == 3 || T == 4) && NEXT) {
-          // lo halves of stage s+1 into registers, one fragment every other
-          // MFMA of steps 3 and 4
+          // lo halves of stage s+1 into registers over the 2Q MFMAs of steps
+          // 3 and 4: one fragment every other MFMA, or every MFMA when a step
+          // has fewer MFMAs than fragments
           constexpr int SL = (T - 3) * Q + I;
-          if constexpr (SL % 2 == 0 && SL / 2 < NF)
-            nlo[SL / 2] = read_lo(nib_base(s + 1, SL / 2), sc_base(s + 1, SL / 2), frag_row(SL / 2), lg);
+          if constexpr (NF <= Q) {
+            if constexpr (SL % 2 == 0 && SL / 2 < NF)
+              nlo[SL / 2] = read_lo(nib_base(s + 1, SL / 2), sc_base(s + 1, SL / 2), frag_row(SL / 2), lg);
+          } else if constexpr (SL < NF) {
+            nlo[SL] = read_lo(nib_base(s + 1, SL), sc_base(s + 1, SL), frag_row(SL), lg);
+          }
         }
         if constexpr (T >= 3 && T <= 6 && MODE == kFull) {
           // refill the ring: the kLoads direct loads spread over steps 3-6
@@ -477,7 +499,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
           });
         }
         if constexpr (T == 7 && NEXT) {
-          if constexpr (I < NF) nhi[I] = read_hi(nib_base(s + 1, I), frag_row(I), lg);
+          // hi halves of stage s+1: fragments I, I + Q, ... at MFMA I
+          static_for<(NF + Q - 1) / Q>([&](auto kc) {
+            constexpr int F = I + decltype(kc)::value * Q;
+            if constexpr (F < NF) nhi[F] = read_hi(nib_base(s + 1, F), frag_row(F), lg);
+          });
         }
         // the hi reads of the previous stage finished long ago; saying so
         // here keeps the compiler from waiting for them behind newer reads
@@ -565,12 +591,17 @@ hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a, Pa
   // The largest tile that still fills the chip for at least one round (the
   // larger the tile, the fewer dequantisations per MFMA): 256 x 256, then
   // 256 x 128, else 128 x 128 (4x the workgroups of 256 x 256; two fit per
-  // CU).
+  // CU) or, where even those are fewer than the CUs, 128 x 64.
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (M >= 256 && N >= 256 && tiles(256, 256) >= 256)
     return launch_cfg<256, 256, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
   if (M >= 256 && N >= 128 && tiles(256, 128) >= 256)
     return launch_cfg<256, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
+  // fewer than 256 tiles of 128 x 128 leave CUs idle: 128 x 64 tiles as long
+  // as they still fit one round (each CU then also moves fewer operand bytes
+  // than a 128 x 128 tile does)
+  if (tiles(128, 128) < 256 && tiles(128, 64) <= 256)
+    return launch_cfg<128, 64, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
   return launch_cfg<128, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
 }
 

@@ -100,10 +100,12 @@ def test_exhaustive_dequant_identity_wide_tiles(N):
     assert np.array_equal(y, dequantize_ref(b[0], b[1]).T.astype(np.float32))
 
 
-@pytest.mark.parametrize("M,N,K", [(520, 16300, 128), (512, 16384, 256), (130, 5000, 384)])
+@pytest.mark.parametrize("M,N,K", [(520, 16300, 128), (512, 16384, 256), (384, 8000, 256),
+                                   (130, 5000, 384), (256, 1000, 512)])
 def test_mid_m_tile_configs(M, N, K):
-    """Shapes whose tile counts pick the 256 x 128 or 128 x 128 configuration
-    (ragged M and N included)."""
+    """Shapes whose tile counts pick the 256 x 128 (the first two), 128 x 128
+    (the third) or 128 x 64 configuration (the last two: fewer than 256
+    tiles of 128 x 128, at most 256 of 128 x 64), ragged M and N included."""
     need_gpu()
     rng = np.random.default_rng(M + N + K)
     a = (*_rand_packed(rng, M, K, 0x00, 0x7E), np.float32(0.7))
