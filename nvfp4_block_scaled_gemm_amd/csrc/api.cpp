@@ -61,9 +61,14 @@ int gemm_dispatch(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uin
                   const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
                   void* y, int dt, int64_t ld_y, nvfp4::QuantOut qo, hipStream_t st) {
   const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
-  // K == 0: the sum is empty; the general kernel writes zeros.
-  if (K > 0 && M <= 128 && tiled_ok(K, a_q, a_s, 256) && tiled_ok(K, b_q, b_s, 256) &&
-      offsets32_ok(N, K))
+  // K == 0: the sum is empty; the general kernel writes zeros.  97-128 rows
+  // go to the MFMA kernel's 64 x 64 tiles when those fill the chip (one
+  // pass over W, ~38 us at N = K = 8192 whatever M), else to the decode
+  // kernel's two 64-row passes, whose second pass costs less the fewer
+  // rows it has (34 / 39 / 47 us at M = 65 / 96 / 128).
+  const bool mid_mfma = M > 96 && ((M + 63) / 64) * ((N + 63) / 64) >= 256;
+  if (K > 0 && M <= 128 && !mid_mfma && tiled_ok(K, a_q, a_s, 256) &&
+      tiled_ok(K, b_q, b_s, 256) && offsets32_ok(N, K))
     return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st, qo));
   if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128) &&
       offsets32_ok(M, K) && offsets32_ok(N, K))

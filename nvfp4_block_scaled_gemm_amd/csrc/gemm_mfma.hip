@@ -539,7 +539,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   const bool whole = y_bytes != 0 && m0 + BM <= M && n0 + BN <= N;
   const bool vec = (y_flags & 1) != 0;
   const int row0 = m0 + wm * C::TM, col0 = n0 + wn * C::TN;
-  constexpr int kRegion = C::TM * (C::TN * 2 + 16);
+  // a wave's staging region: its bf16 tile, or half its fp32 tile (a
+  // 32-row fp32 pass when the tile is 32 rows tall) for the NVFP4 encoder
+  constexpr int kRegionBf16 = C::TM * (C::TN * 2 + 16);
+  constexpr int kRegionQuant = (C::FM >= 2 ? C::FM / 2 : 1) * 32 * (C::TN * 4 + 16);
+  constexpr int kRegion = kRegionBf16 > kRegionQuant ? kRegionBf16 : kRegionQuant;
   static_assert(C::kWaves * kRegion <= kStages * L::kBytes, "epilogue staging exceeds the ring");
   workgroup_barrier();
   uint8_t* region = smem + wave * kRegion;
@@ -590,19 +594,20 @@ hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a, Pa
                             void* y, int y_dtype, int64_t ld_y, hipStream_t stream, QuantOut qo) {
   // The largest tile that still fills the chip for at least one round (the
   // larger the tile, the fewer dequantisations per MFMA): 256 x 256, then
-  // 256 x 128, else 128 x 128 (4x the workgroups of 256 x 256; two fit per
-  // CU) or, where even those are fewer than the CUs, 128 x 64.
+  // 256 x 128, then 128 x 128 (4x the workgroups of 256 x 256).  Below that,
+  // smaller tiles keep every CU busy and move fewer operand bytes per CU:
+  // 128 x 64 while it fits one round (else one round of 128 x 128), then
+  // 64 x 64 while that fits one round.
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (M >= 256 && N >= 256 && tiles(256, 256) >= 256)
     return launch_cfg<256, 256, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
   if (M >= 256 && N >= 128 && tiles(256, 128) >= 256)
     return launch_cfg<256, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
-  // fewer than 256 tiles of 128 x 128 leave CUs idle: 128 x 64 tiles as long
-  // as they still fit one round (each CU then also moves fewer operand bytes
-  // than a 128 x 128 tile does)
-  if (tiles(128, 128) < 256 && tiles(128, 64) <= 256)
+  if (tiles(128, 128) >= 256 || tiles(128, 64) > 256)
+    return launch_cfg<128, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
+  if (tiles(128, 64) == 256 || tiles(64, 64) > 256)
     return launch_cfg<128, 64, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
-  return launch_cfg<128, 128, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
+  return launch_cfg<64, 64, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
 }
 
 }  // namespace nvfp4

@@ -101,11 +101,16 @@ def test_exhaustive_dequant_identity_wide_tiles(N):
 
 
 @pytest.mark.parametrize("M,N,K", [(520, 16300, 128), (512, 16384, 256), (384, 8000, 256),
-                                   (130, 5000, 384), (256, 1000, 512)])
+                                   (256, 8192, 512), (200, 8100, 384),
+                                   (130, 5000, 384), (100, 8192, 256), (70, 8150, 384)])
 def test_mid_m_tile_configs(M, N, K):
-    """Shapes whose tile counts pick the 256 x 128 (the first two), 128 x 128
-    (the third) or 128 x 64 configuration (the last two: fewer than 256
-    tiles of 128 x 128, at most 256 of 128 x 64), ragged M and N included."""
+    """Shapes whose tile counts pick each MFMA tile configuration, ragged M
+    and N included.  The first two pick 256 x 128, the third 128 x 128.
+    The next two pick 128 x 64 (fewer than 256 tiles of 128 x 128, at most
+    256 of 128 x 64, or more than 256 of 64 x 64).  The last three pick
+    64 x 64.  Of those, (100, 8192) has more than 96 rows and 64 x 64 tiles
+    that fill the chip, so the MFMA kernel takes it over from the decode
+    kernel's two passes; (70, 8150) gets there because K % 256 != 0."""
     need_gpu()
     rng = np.random.default_rng(M + N + K)
     a = (*_rand_packed(rng, M, K, 0x00, 0x7E), np.float32(0.7))
