@@ -124,7 +124,8 @@ def test_mid_m_tile_configs(M, N, K):
 
 @pytest.mark.parametrize("M,N", [(65, 96), (100, 40), (128, 200)])
 def test_decode_two_passes(M, N):
-    """65 <= M <= 128 runs the weight-streaming kernel in two 64-row passes."""
+    """65 <= M <= 128 runs the weight-streaming kernel in two 64-row passes
+    when 64 x 64 MFMA tiles would not fill the chip (small N here)."""
     need_gpu()
     K = 512
     rng = np.random.default_rng(M + N)
