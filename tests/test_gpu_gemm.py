@@ -303,3 +303,48 @@ def test_bf16_output_rne_at_the_extremes(M, N, K, ga, gb):
     y16 = _gemm(a, b, "bf16")
     ref = y32.cpu().to(torch.bfloat16)
     assert torch.equal(ref.view(torch.int16), y16.cpu().view(torch.int16))
+
+
+def test_operands_beyond_4_gib():
+    """Maximum sizes: a 600000 x 16384 operand packs to 4.9 GB, so its byte
+    offsets pass 2^31 and 2^32.  The quantiser walks it with 64-bit offsets,
+    and the GEMM sends it to the general kernel both as A (against 40 weight
+    rows, f32 out) and as W (under 3 activation rows, bf16 out).  Rows repeat
+    a seeded 1000-row block; 1000 divides neither 2^31 nor 2^32 bytes' worth
+    of rows (8192 bytes each), so an offset that wrapped would read another
+    block row.  Rows on both sides of those offsets, the last rows and a
+    random sample are checked: quantised bytes exactly, GEMM outputs to the
+    tolerance."""
+    need_gpu()
+    rows, K, period = 600000, 16384, 1000
+    block = wl.randn((period, K), 8101, "bf16")
+    g = oracle_global_scale(block)                   # the tensor's amax is the block's
+    note(f"quantise {rows} x {K} bf16 ({rows * K * 2 / 1e9:.1f} GB)")
+    x = block.cuda().repeat(rows // period, 1)
+    big = nv.nvfp4_quantize(x)
+    torch.cuda.synchronize()
+    del x
+    torch.cuda.empty_cache()
+    per_row = K // 2
+    edges = [0, 1, (1 << 31) // per_row - 1, (1 << 31) // per_row,
+             (1 << 32) // per_row - 1, (1 << 32) // per_row, rows - 2, rows - 1]
+    rng = np.random.default_rng(8102)
+    sample = np.unique(np.concatenate([edges, rng.choice(rows, 8, replace=False)]))
+    idx = torch.from_numpy(sample).cuda()
+    ra = oracle_quantize(block[torch.from_numpy(sample % period)], g)
+    assert_bytes_equal(big[0][idx], big[1][idx], big[2], *ra)
+
+    rb = oracle_quantize(wl.randn((40, K), 8103, "bf16"))
+    note(f"gemm A beyond 4 GiB M={rows} N=40 K={K} (general kernel)")
+    y = _gemm(big, to_gpu(*rb), "f32")
+    y_ref, bound = gemm_ref(*ra, *rb)
+    ok, worst = check_gemm(np_(y[idx]), y_ref, bound, "f32")
+    assert ok, f"A beyond 4 GiB: worst |err|/tol = {worst}"
+    del y
+
+    rx = oracle_quantize(wl.randn((3, K), 8104, "bf16"))
+    note(f"gemm W beyond 4 GiB M=3 N={rows} K={K} (general kernel)")
+    y = _gemm(to_gpu(*rx), big, "bf16")
+    y_ref, bound = gemm_ref(*rx, *ra)
+    ok, worst = check_gemm(np_(y[:, idx]), y_ref, bound, "bf16")
+    assert ok, f"W beyond 4 GiB: worst |err|/tol = {worst}"
