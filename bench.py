@@ -20,7 +20,10 @@ issues.  ``decode`` holds the skinny M = 1, 16, 32 GEMMs over 16 rotating copies
 back-to-back launches between one pair of events, and ``moe_grouped``
 the two grouped expert GEMMs, each against HBM peak; ``mid_m`` GEMMs with
 M = 64 .. 1024 on the same rotating weights; ``large`` the
-M = N = K = 16384 outlier workload (quantiser on x alone, then the GEMM).
+M = N = K = 16384 outlier workload (quantiser on x alone, then the GEMM);
+``library_reference`` torch's bf16 GEMM at the linear shape and a 1 GiB
+device copy on the same box, as context for what the hardware gives a
+plain dense GEMM and a plain stream.
 ``cpu_baseline`` times the CPU oracle on a bounded row slice of the same step.
 """
 from __future__ import annotations
@@ -433,6 +436,27 @@ def main():
              "gemm_frac_mfma": round(lflop / (lg_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4)}
     del xl, wlq, xlq, yl
 
+    # Context only, not a denominator: what the platform's own libraries reach
+    # on the same box.  torch's bf16 GEMM (hipBLASLt) at the linear shape,
+    # y = x . W^T with W^T made contiguous beforehand, and a 1 GiB device
+    # copy (bytes read + bytes written).
+    wt = w.t().contiguous()
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    timed_batch(lambda i: torch.mm(x, wt, out=yb), 5)
+    mm_ms = timed_batch(lambda i: torch.mm(x, wt, out=yb), 20)
+    del wt, yb
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    timed_batch(lambda i: cdst.copy_(csrc), 2)
+    cp_ms = timed_batch(lambda i: cdst.copy_(csrc), 10)
+    cp_gbs = 2 * csrc.numel() * 4 / (cp_ms * 1e-3) / 1e9
+    del csrc, cdst
+    library = {"bf16_gemm_torch_linear_us": round(mm_ms * 1e3, 2),
+               "bf16_gemm_torch_linear_tflops": round(flop / (mm_ms * 1e-3) / 1e12, 1),
+               "nvfp4_gemm_over_bf16_gemm_speed": round(mm_ms / gemm_ms, 3),
+               "copy_1gib_GBps": round(cp_gbs, 1),
+               "copy_frac_hbm": round(cp_gbs / PEAK_HBM_GBS, 4)}
+
     out = {
         "metric": "NVFP4 GEMM TFLOPS + % of MFMA/HBM roofline (M=4096,N=K=8192; M=16 decode)",
         "value": round(value, 2),
@@ -462,6 +486,7 @@ def main():
         "fused_quant_out": fused,
         "mfma_sustained_probe": probe_ref,
         "mid_m": dict(mid_m, workload="m{64..1024}_n8192_k8192, 16 rotating weight copies"),
+        "library_reference": library,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, args.cpu_rows)
