@@ -78,9 +78,11 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
     const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
     const float* __restrict__ b_g, const int32_t* __restrict__ m_offsets, int32_t G,
     const int32_t* __restrict__ row_index, int64_t a_rows, void* __restrict__ y, int y_dtype,
-    int64_t ld_y, QuantOut qo) {
+    int64_t ld_y, QuantOut qo, int64_t m_base) {
+  // rows m_base + blockIdx.y * 16 + ... of the whole problem (grid.y is
+  // limited, so large M is launched in row chunks)
   const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
-  const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int64_t m = m_base + (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
   const bool in = m < M && n < N;
   if (!in && y_dtype != 2) return;  // the NVFP4 writer needs every thread at its barrier
   const float v = in ? dot(M, N, K, a_q, a_s, b_q, b_s, m_offsets, G, row_index, a_rows, m, n,
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   tile[threadIdx.x >> 4][threadIdx.x & 15] = v;
   __syncthreads();
   if (threadIdx.x < 16) {
-    const int64_t row = (int64_t)blockIdx.y * 16 + threadIdx.x, c0 = (int64_t)blockIdx.x * 16;
+    const int64_t row = m_base + (int64_t)blockIdx.y * 16 + threadIdx.x, c0 = (int64_t)blockIdx.x * 16;
     const float g = qo.g[0];
     const enc::EncodeParams P = enc::make_params(g);
     const int mode = enc::encode_mode(g);
@@ -116,24 +118,16 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
 hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                   const int32_t* m_offsets, int32_t G, const int32_t* row_index, int64_t a_rows,
                   void* y, int y_dtype, int64_t ld_y, hipStream_t stream, QuantOut qo) {
-  // grid.y is limited to 65535 row tiles; larger M is split into chunks
+  // grid.y is limited to 65535 row tiles; larger M is launched in row
+  // chunks, each told its first row (pointers stay those of the whole
+  // problem, so the group search and the row index see global rows)
   const int64_t max_rows = 65535LL * 16;
   for (int64_t m0 = 0; m0 < M; m0 += max_rows) {
     const int64_t rows = (M - m0 < max_rows) ? (M - m0) : max_rows;
     dim3 grid((unsigned)((N + 15) / 16), (unsigned)((rows + 15) / 16));
-    // chunks past the first shift A and y; the group search sees global rows
-    // only through m_offsets, so chunking is used for the dense case alone
-    QuantOut qc = qo;
-    if (y_dtype == 2) {
-      qc.q += m0 * (N / 2);
-      qc.s += m0 * (N / 16);
-    }
-    gemm_generic_kernel<<<grid, 256, 0, stream>>>(
-        rows, N, K, a.q + m0 * (K / 2), a.s + m0 * (K / 16), a.g, b.q, b.s, b.g, m_offsets, G,
-        row_index, a_rows,
-        y_dtype == 2 ? y
-                     : (y_dtype == 0 ? (void*)((float*)y + m0 * ld_y) : (void*)((uint16_t*)y + m0 * ld_y)),
-        y_dtype, ld_y, qc);
+    gemm_generic_kernel<<<grid, 256, 0, stream>>>(M, N, K, a.q, a.s, a.g, b.q, b.s, b.g,
+                                                   m_offsets, G, row_index, a_rows, y, y_dtype,
+                                                   ld_y, qo, m0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -152,7 +146,6 @@ hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets,
                                        const int32_t* row_index, int64_t total_m, int64_t a_rows,
                                        int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                                        void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
-  if (total_m > 65535LL * 16) return hipErrorInvalidValue;
   return launch(total_m, N, K, a, b, m_offsets, G, row_index,
                 row_index != nullptr ? a_rows : total_m, y, y_dtype, ld_y, stream, QuantOut{});
 }

@@ -348,3 +348,34 @@ def test_operands_beyond_4_gib():
     y_ref, bound = gemm_ref(*rx, *ra)
     ok, worst = check_gemm(np_(y[:, idx]), y_ref, bound, "bf16")
     assert ok, f"W beyond 4 GiB: worst |err|/tol = {worst}"
+
+
+def test_general_kernel_past_its_row_chunks():
+    """Dense calls with K = 48 run the general kernel, which launches at most
+    1,048,560 rows at a time: 1,100,000 rows (a seeded 1000-row block
+    repeated) cross that boundary.  The fp32 output is checked on rows
+    around it, the last rows and a random sample; the NVFP4 output of the
+    same call equals the oracle's quantisation of that fp32 output under the
+    same static scale on those rows."""
+    need_gpu()
+    M, K, N, period = 1_100_000, 48, 32, 1000
+    ra = oracle_quantize(wl.randn((period, K), 8301, "bf16"))
+    rb = oracle_quantize(wl.randn((N, K), 8302, "bf16"))
+    a_small = to_gpu(*ra)
+    a = (a_small[0].repeat(M // period, 1), a_small[1].repeat(M // period, 1), a_small[2])
+    rng = np.random.default_rng(8303)
+    rows = np.unique(np.concatenate([[0, 1_048_559, 1_048_560, 1_048_561, M - 2, M - 1],
+                                     rng.choice(M, 8, replace=False)]))
+    idx = torch.from_numpy(rows).cuda()
+    note(f"dense general kernel M={M} N={N} K={K}")
+    y = _gemm(a, to_gpu(*rb), "f32")
+    y_rows = np_(y[idx])
+    y_ref, bound = gemm_ref(ra[0][rows % period], ra[1][rows % period], ra[2], *rb)
+    ok, worst = check_gemm(y_rows, y_ref, bound, "f32")
+    assert ok, worst
+    g = torch.tensor([float(np.abs(y_rows).max() / 2688.0)], dtype=torch.float32, device="cuda")
+    note(f"dense general kernel, NVFP4 output, M={M}")
+    q, s, _ = nv.nvfp4_gemm_nvfp4_out(a, to_gpu(*rb), g)
+    torch.cuda.synchronize()
+    ref = oracle_quantize(torch.from_numpy(y_rows), np.float32(g.item()))
+    assert_bytes_equal(q[idx], s[idx], g, *ref)

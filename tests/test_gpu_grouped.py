@@ -260,3 +260,59 @@ def test_skewed_routing(K, N):
     torch.cuda.synchronize()
     ok, worst = check_gemm(np_(y), y_ref, bound, "bf16")
     assert ok, worst
+
+
+def test_general_kernel_past_its_row_chunks():
+    """The general kernel launches at most 1,048,560 rows (65535 row tiles of
+    16) at a time; larger problems run in row chunks that see global rows.
+    K = 256 sends grouped calls to it.  1,100,000 grouped rows in 4 groups
+    (one empty, one straddling the first chunk boundary), rows repeating a
+    seeded 1000-row block; then the same through a routing index with
+    repeated and out-of-range entries.  Rows at the chunk and group
+    boundaries, the last rows and a random sample are checked."""
+    need_gpu()
+    total, K, N, period = 1_100_000, 256, 16, 1000
+    bounds = [0, 500_000, 500_000, 1_048_570, total]
+    ra = oracle_quantize(wl.randn((period, K), 8201, "bf16"))
+    rbs = [oracle_quantize(wl.randn((N, K), 8202 + e, "bf16")) for e in range(4)]
+    dev = "cuda"
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)  # noqa: E731
+    off = torch.tensor(bounds, dtype=torch.int32, device=dev)
+    b = (t(np.stack([r[0] for r in rbs])), t(np.stack([r[1] for r in rbs])),
+         t(np.array([r[2] for r in rbs], dtype=np.float32)))
+    a_g = torch.tensor([float(ra[2])], device=dev)
+    reps = total // period
+    a_full = (t(ra[0]).repeat(reps, 1), t(ra[1]).repeat(reps, 1), a_g)
+    rng = np.random.default_rng(8210)
+    rows = np.unique(np.concatenate([[0, 499_999, 500_000, 1_048_559, 1_048_560, 1_048_561,
+                                      1_048_569, 1_048_570, total - 1],
+                                     rng.choice(total, 8, replace=False)]))
+    group = np.searchsorted(np.array(bounds), rows, side="right") - 1
+
+    def check(y, src_rows):
+        y_np = np_(y[torch.from_numpy(rows).to(dev)])
+        for e in range(4):
+            sel = group == e
+            if not sel.any():
+                continue
+            src = src_rows[sel]
+            ok_rows = (src >= 0) & (src < period)
+            qa = np.where(ok_rows[:, None], ra[0][np.clip(src, 0, period - 1)], 0).astype(np.uint8)
+            sa = np.where(ok_rows[:, None], ra[1][np.clip(src, 0, period - 1)], 0).astype(np.uint8)
+            y_ref, bound = gemm_ref(qa, sa, ra[2], *rbs[e])
+            ok, worst = check_gemm(y_np[sel], y_ref, bound, "f32")
+            assert ok, f"group {e}: worst |err|/tol = {worst}"
+
+    note(f"grouped general kernel total={total} K={K} N={N}")
+    y = nv.nvfp4_grouped_gemm(off, total, a_full, b, out_dtype="f32")
+    torch.cuda.synchronize()
+    check(y, rows % period)
+    del y, a_full
+
+    idx = (np.arange(total, dtype=np.int64) * 7919) % period
+    idx[[1_048_560, total - 1]] = [-1, period]               # read as zero rows
+    note(f"grouped general kernel through the index total={total} a_rows={period}")
+    y = nv.nvfp4_grouped_gemm(off, total, (t(ra[0]), t(ra[1]), a_g), b, out_dtype="f32",
+                              row_index=t(idx.astype(np.int32)))
+    torch.cuda.synchronize()
+    check(y, idx[rows])
