@@ -89,6 +89,39 @@ _DT_IN = {torch.float32: NVFP4_F32, torch.bfloat16: NVFP4_BF16}
 _DT_OUT = {"f32": (NVFP4_F32, torch.float32), "bf16": (NVFP4_BF16, torch.bfloat16)}
 
 
+# The library reads packed operands as row-major [rows, K/2] and [rows, K/16]
+# bytes and writes outputs of the dtype it is told; these checks keep a
+# mismatched tensor from reaching it (they raise before any GPU work).
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(dev, *ts):
+    for t in ts:
+        _need(t.is_cuda and t.device == dev, f"tensors must all be on {dev}")
+
+
+def _packed(t3, rows: int, K: int, what: str, n_g: int = 1):
+    """(q, s, g) of a packed operand [.., rows, K]: uint8 q [.., rows, K/2] and
+    s [.., rows, K/16], contiguous; fp32 g with n_g elements."""
+    q, s, g = t3
+    lead = tuple(q.shape[:-2])
+    _need(q.dtype == torch.uint8 and s.dtype == torch.uint8, f"{what}: q and s must be uint8")
+    _need(tuple(q.shape) == (*lead, rows, K // 2) and tuple(s.shape) == (*lead, rows, K // 16),
+          f"{what}: q {tuple(q.shape)} and s {tuple(s.shape)} do not pack [{rows}, {K}]")
+    _need(q.is_contiguous() and s.is_contiguous(), f"{what}: q and s must be contiguous")
+    _need(g.dtype == torch.float32 and g.numel() == n_g and g.is_contiguous(),
+          f"{what}: g must be {n_g} contiguous fp32 value(s)")
+
+
+def _out(y, rows: int, cols: int, dtype, what: str = "y"):
+    _need(y.dtype == dtype, f"{what}: dtype {y.dtype}, expected {dtype}")
+    _need(y.dim() == 2 and tuple(y.shape) == (rows, cols), f"{what}: shape {tuple(y.shape)}, "
+          f"expected ({rows}, {cols})")
+    _need(y.stride(1) == 1 or cols <= 1, f"{what}: rows must have unit column stride")
+
+
 # --------------------------------------------------------------------------
 # raw entry points (same names and arguments as the C ABI)
 # --------------------------------------------------------------------------
@@ -137,15 +170,26 @@ def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None,
     """x [rows, cols] fp32/bf16 on the GPU -> (q uint8 [rows, cols/2],
     s uint8 [rows, cols/16], g fp32 [1]).  ``global_scale`` (device fp32 [1])
     switches to the static-scale path; ``out`` = (q, s, g) reuses buffers."""
-    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1, "x: 2-D, unit column stride, on GPU"
+    _need(x.dim() == 2 and x.dtype in _DT_IN, "x: 2-D fp32 or bf16")
+    _need(x.stride(1) == 1 or x.shape[1] <= 1, "x: rows must have unit column stride")
     rows, cols = x.shape
+    _need(cols % 16 == 0, "x: columns must be a multiple of 16")
     dev = x.device
     if out is None:
+        _on_gpu(dev, x)
         q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
         s = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
         g = torch.empty(1, dtype=torch.float32, device=dev)
     else:
         q, s, g = out
+        _packed((q, s, g), rows, cols, "out")
+    if global_scale is not None:
+        _need(global_scale.dtype == torch.float32 and global_scale.numel() == 1,
+              "global_scale: one fp32 value")
+        _on_gpu(dev, global_scale)
+    if workspace is not None:
+        _on_gpu(dev, workspace)
+    _on_gpu(dev, x, q, s, g)
     flags = 0
     if global_scale is not None:
         g.copy_(global_scale.reshape(1))
@@ -165,11 +209,16 @@ def nvfp4_gemm(a, b, out_dtype: str = "bf16", y: torch.Tensor | None = None, str
     """a = (q, s, g) of x [M, K]; b = (q, s, g) of W [N, K] -> y [M, N]."""
     a_q, a_s, a_g = a
     b_q, b_s, b_g = b
+    _need(a_q.dim() == 2 and b_q.dim() == 2, "a and b: 2-D packed operands")
     M, N, K = a_q.shape[0], b_q.shape[0], a_q.shape[1] * 2
-    assert b_q.shape[1] * 2 == K and a_s.shape == (M, K // 16) and b_s.shape == (N, K // 16)
+    _packed(a, M, K, "a")
+    _packed(b, N, K, "b")
+    _need(out_dtype in _DT_OUT, f"out_dtype: one of {sorted(_DT_OUT)}")
     code, tdt = _DT_OUT[out_dtype]
     if y is None:
         y = torch.empty((M, N), dtype=tdt, device=a_q.device)
+    _out(y, M, N, tdt)
+    _on_gpu(a_q.device, a_q, a_s, a_g, b_q, b_s, b_g, y)
     st = nvfp4_gemm_raw(M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s),
                         _ptr(b_g), _ptr(y), code, y.stride(0), stream)
     _check("nvfp4_gemm", st)
@@ -182,13 +231,18 @@ def nvfp4_gemm_nvfp4_out(a, b, y_g: torch.Tensor, out=None, stream=None):
     quantised in the GEMM's epilogue.  ``out`` = (q, s) reuses buffers."""
     a_q, a_s, a_g = a
     b_q, b_s, b_g = b
+    _need(a_q.dim() == 2 and b_q.dim() == 2, "a and b: 2-D packed operands")
     M, N, K = a_q.shape[0], b_q.shape[0], a_q.shape[1] * 2
-    assert b_q.shape[1] * 2 == K and y_g.dtype == torch.float32 and y_g.numel() == 1
+    _packed(a, M, K, "a")
+    _packed(b, N, K, "b")
+    _need(N % 16 == 0, "the output's columns (rows of b) must be a multiple of 16")
     if out is None:
         q = torch.empty((M, N // 2), dtype=torch.uint8, device=a_q.device)
         s = torch.empty((M, N // 16), dtype=torch.uint8, device=a_q.device)
     else:
         q, s = out
+    _packed((q, s, y_g), M, N, "out")
+    _on_gpu(a_q.device, a_q, a_s, a_g, b_q, b_s, b_g, q, s, y_g)
     st = nvfp4_gemm_nvfp4_out_raw(M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q),
                                   _ptr(b_s), _ptr(b_g), _ptr(q), _ptr(s), _ptr(y_g), stream)
     _check("nvfp4_gemm_nvfp4_out", st)
@@ -204,19 +258,28 @@ def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: s
     row_index[r] of a = (q [a_rows, K/2], s, g) instead (no gathered copy)."""
     a_q, a_s, a_g = a
     b_q, b_s, b_g = b
+    _need(b_q.dim() == 3 and a_q.dim() == 2, "b: [G, N, K/2] packed experts; a: 2-D packed rows")
     G, N = b_q.shape[0], b_q.shape[1]
     K = b_q.shape[2] * 2
-    assert m_offsets.dtype == torch.int32 and m_offsets.numel() == G + 1
+    _packed(b, N, K, "b", n_g=G)
+    _packed(a, a_q.shape[0] if row_index is not None else total_m, K, "a")
+    _need(m_offsets.dtype == torch.int32 and m_offsets.numel() == G + 1
+          and m_offsets.is_contiguous(), "m_offsets: G + 1 contiguous int32")
+    _need(out_dtype in _DT_OUT, f"out_dtype: one of {sorted(_DT_OUT)}")
     code, tdt = _DT_OUT[out_dtype]
     if y is None:
         y = torch.empty((total_m, N), dtype=tdt, device=b_q.device)
+    _out(y, total_m, N, tdt)
+    _on_gpu(b_q.device, a_q, a_s, a_g, b_q, b_s, b_g, m_offsets, y)
     if row_index is None:
         st = nvfp4_grouped_gemm_raw(G, _ptr(m_offsets), total_m, N, K, _ptr(a_q), _ptr(a_s),
                                     _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
                                     y.stride(0), stream)
         _check("nvfp4_grouped_gemm", st)
         return y
-    assert row_index.dtype == torch.int32 and row_index.numel() == total_m
+    _need(row_index.dtype == torch.int32 and row_index.numel() == total_m
+          and row_index.is_contiguous(), "row_index: total_m contiguous int32")
+    _on_gpu(b_q.device, row_index)
     st = nvfp4_grouped_gemm_gather_raw(G, _ptr(m_offsets), _ptr(row_index), total_m,
                                        a_q.shape[0], N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g),
                                        _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,

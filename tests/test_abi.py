@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import nvfp4_block_scaled_gemm_amd as nv
 
@@ -193,3 +194,54 @@ def _gq(**kw):
 ])
 def test_gemm_nvfp4_out_argument_checks(kw, status):
     assert _gq(**kw) == status
+
+
+def _packed_cpu(rows, K, n_g=1):
+    return (torch.zeros((rows, K // 2), dtype=torch.uint8),
+            torch.zeros((rows, K // 16), dtype=torch.uint8),
+            torch.ones(n_g, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("case", ["y_dtype", "y_shape", "a_noncontig", "b_scale_shape",
+                                  "g_dtype", "out_dtype", "cpu_tensors"])
+def test_binding_rejects_mismatched_tensors(case):
+    """The tensor wrappers check what the C ABI cannot see (dtypes, shapes,
+    packing, device) and raise before any library call or GPU work."""
+    M, N, K = 4, 32, 64
+    a, b = _packed_cpu(M, K), _packed_cpu(N, K)
+    kw = {}
+    if case == "y_dtype":
+        kw = dict(out_dtype="f32", y=torch.empty((M, N), dtype=torch.bfloat16))
+    elif case == "y_shape":
+        kw = dict(y=torch.empty((M, N + 1), dtype=torch.bfloat16))
+    elif case == "a_noncontig":
+        wide = torch.zeros((M, K), dtype=torch.uint8)
+        a = (wide[:, : K // 2], a[1], a[2])
+    elif case == "b_scale_shape":
+        b = (b[0], torch.zeros((N, K // 8), dtype=torch.uint8), b[2])
+    elif case == "g_dtype":
+        a = (a[0], a[1], torch.ones(1, dtype=torch.float64))
+    elif case == "out_dtype":
+        kw = dict(out_dtype="fp8")
+    with pytest.raises(ValueError):
+        nv.nvfp4_gemm(a, b, **kw)
+
+
+def test_binding_rejects_mismatched_quantize_and_grouped_tensors():
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize(torch.zeros((4, 32), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize(torch.zeros((4, 40), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize(torch.zeros((4, 32)), out=_packed_cpu(4, 64))
+    G, N, K, total = 3, 16, 64, 10
+    bq = torch.zeros((G, N, K // 2), dtype=torch.uint8)
+    bs = torch.zeros((G, N, K // 16), dtype=torch.uint8)
+    b = (bq, bs, torch.ones(G))
+    a = _packed_cpu(total, K)
+    with pytest.raises(ValueError):   # int64 offsets
+        nv.nvfp4_grouped_gemm(torch.zeros(G + 1, dtype=torch.int64), total, a, b)
+    with pytest.raises(ValueError):   # one global scale for three experts
+        nv.nvfp4_grouped_gemm(torch.zeros(G + 1, dtype=torch.int32), total, a, (bq, bs, torch.ones(1)))
+    with pytest.raises(ValueError):   # CPU tensors
+        nv.nvfp4_grouped_gemm(torch.zeros(G + 1, dtype=torch.int32), total, a, b)
