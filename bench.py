@@ -247,7 +247,8 @@ def main():
 
     # skinny decode GEMMs (M = 1, 16, 32) over 16 rotating weight copies
     # (604 MB, more than the 256 MB Infinity Cache holds: cache-cold W)
-    copies = [tuple(t.clone() for t in wq) for _ in range(16)]
+    # weights quantised ahead of time are held as checked Packed operands
+    copies = [nv.Packed(tuple(t.clone() for t in wq)) for _ in range(16)]
 
     def timed(fn, reps):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -374,11 +375,13 @@ def main():
                          sk.m_offsets.to(dev), int(sk.m_offsets[-1])))
             moe["skewed_router"] = {"skew": 1.0, "experts_used": int((sk.counts > 0).sum()),
                                     "rows_per_expert_max": int(sk.counts.max())}
+        experts = nv.Packed((bq, bs, bg))
         for name, a_op, ri, off_, tot_ in runs:
+            a_op = nv.Packed(tuple(a_op))
             # ~20-30 ms of untimed launches first: clocks settle under a new load
-            timed(lambda i: nv.nvfp4_grouped_gemm(off_, tot_, a_op, (bq, bs, bg), "bf16", y=ym,
+            timed(lambda i: nv.nvfp4_grouped_gemm(off_, tot_, a_op, experts, "bf16", y=ym,
                                                   row_index=ri), 40)
-            ms = timed(lambda i: nv.nvfp4_grouped_gemm(off_, tot_, a_op, (bq, bs, bg), "bf16",
+            ms = timed(lambda i: nv.nvfp4_grouped_gemm(off_, tot_, a_op, experts, "bf16",
                                                        y=ym, row_index=ri), 20)
             # weights of the experts that have rows (each read once), their rows, y
             used = int((torch.diff(off_.cpu().to(torch.int64)) > 0).sum())
@@ -387,7 +390,7 @@ def main():
             moe[name] = {"N": n_, "K": k_, "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
                          "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "tflops": round(2.0 * tot_ * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
-        del bq, bs, bg, a, ym
+        del bq, bs, bg, a, ym, experts, a_op
 
     # Same-box reference for the dense GEMM: the sustained rate of pure fp16
     # MFMAs on every CU (the probe of --mode mfma_rate, no memory traffic,

@@ -76,13 +76,23 @@ def _check(fn: str, status: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # the pointer arguments are declared c_void_p, so a plain int is passed
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream=None):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream=None, dev: int | None = None):
+    """HIP stream handle: ``stream`` (a torch stream or a raw handle), else the
+    current stream of device ``dev`` (default: the current device)."""
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    if dev is None:
+        dev = torch.cuda.current_device()
+    if _raw_stream is not None:
+        return _raw_stream(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 _DT_IN = {torch.float32: NVFP4_F32, torch.bfloat16: NVFP4_BF16}
@@ -91,35 +101,64 @@ _DT_OUT = {"f32": (NVFP4_F32, torch.float32), "bf16": (NVFP4_BF16, torch.bfloat1
 
 # The library reads packed operands as row-major [rows, K/2] and [rows, K/16]
 # bytes and writes outputs of the dtype it is told; these checks keep a
-# mismatched tensor from reaching it (they raise before any GPU work).
+# mismatched tensor from reaching it (they raise before any GPU work).  A
+# packed operand is checked once, when it becomes a ``Packed``, so that the
+# per-call cost stays small next to a few-microsecond decode GEMM.
 def _need(cond: bool, msg: str):
     if not cond:
         raise ValueError(msg)
 
 
-def _on_gpu(dev, *ts):
-    for t in ts:
-        _need(t.is_cuda and t.device == dev, f"tensors must all be on {dev}")
+class Packed(tuple):
+    """(q, s, g) of an NVFP4 tensor [rows, K], or of G expert weights
+    [G, rows, K]: uint8 q [.., rows, K/2] and s [.., rows, K/16], both
+    contiguous, and fp32 g (one value, or one per expert), all on one GPU.
+    Checked when made; nvfp4_quantize returns one.  Changing the tensors'
+    shapes in place afterwards is not supported."""
+
+    def __new__(cls, ts, _trusted=None):
+        q, s, g = ts
+        self = super().__new__(cls, (q, s, g))
+        if _trusted is not None:
+            self.lead, self.rows, self.K, self.dev = _trusted
+            return self
+        _need(q.dim() >= 2, "q: at least 2-D")
+        lead = tuple(q.shape[:-2])
+        rows, K = q.shape[-2], q.shape[-1] * 2
+        _need(q.dtype == torch.uint8 and s.dtype == torch.uint8, "q and s must be uint8")
+        _need(tuple(s.shape) == (*lead, rows, K // 16) and K % 16 == 0,
+              f"q {tuple(q.shape)} and s {tuple(s.shape)} do not pack [{rows}, {K}]")
+        _need(q.is_contiguous() and s.is_contiguous(), "q and s must be contiguous")
+        n_g = lead[0] if len(lead) == 1 else 1
+        _need(len(lead) <= 1, "at most one leading (expert) dimension")
+        _need(g.dtype == torch.float32 and g.numel() == n_g and g.is_contiguous(),
+              f"g must be {n_g} contiguous fp32 value(s)")
+        dev = q.get_device()
+        _need(q.is_cuda and s.get_device() == dev and g.get_device() == dev,
+              "q, s and g must be on one GPU")
+        self.lead, self.rows, self.K, self.dev = lead, rows, K, dev
+        return self
 
 
-def _packed(t3, rows: int, K: int, what: str, n_g: int = 1):
-    """(q, s, g) of a packed operand [.., rows, K]: uint8 q [.., rows, K/2] and
-    s [.., rows, K/16], contiguous; fp32 g with n_g elements."""
-    q, s, g = t3
-    lead = tuple(q.shape[:-2])
-    _need(q.dtype == torch.uint8 and s.dtype == torch.uint8, f"{what}: q and s must be uint8")
-    _need(tuple(q.shape) == (*lead, rows, K // 2) and tuple(s.shape) == (*lead, rows, K // 16),
-          f"{what}: q {tuple(q.shape)} and s {tuple(s.shape)} do not pack [{rows}, {K}]")
-    _need(q.is_contiguous() and s.is_contiguous(), f"{what}: q and s must be contiguous")
-    _need(g.dtype == torch.float32 and g.numel() == n_g and g.is_contiguous(),
-          f"{what}: g must be {n_g} contiguous fp32 value(s)")
+def _packed(t3) -> Packed:
+    return t3 if type(t3) is Packed else Packed(t3)
 
 
-def _out(y, rows: int, cols: int, dtype, what: str = "y"):
+def _out(y, rows: int, cols: int, dtype, dev: int, what: str = "y") -> int:
+    """Checks an output [rows, cols] of ``dtype`` on GPU ``dev``; returns its
+    row stride."""
+    ld, cs = y.stride()
+    if y.dtype == dtype and y.shape == (rows, cols) and (cs == 1 or cols <= 1) \
+            and y.get_device() == dev:
+        return ld
     _need(y.dtype == dtype, f"{what}: dtype {y.dtype}, expected {dtype}")
-    _need(y.dim() == 2 and tuple(y.shape) == (rows, cols), f"{what}: shape {tuple(y.shape)}, "
-          f"expected ({rows}, {cols})")
-    _need(y.stride(1) == 1 or cols <= 1, f"{what}: rows must have unit column stride")
+    _need(y.shape == (rows, cols), f"{what}: shape {tuple(y.shape)}, expected ({rows}, {cols})")
+    _need(cs == 1 or cols <= 1, f"{what}: rows must have unit column stride")
+    raise ValueError(f"{what}: must be on the operands' GPU")
+
+
+def _on_dev(t, dev: int, what: str):
+    _need(t.get_device() == dev, f"{what}: must be on the operands' GPU")
 
 
 # --------------------------------------------------------------------------
@@ -174,22 +213,25 @@ def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None,
     _need(x.stride(1) == 1 or x.shape[1] <= 1, "x: rows must have unit column stride")
     rows, cols = x.shape
     _need(cols % 16 == 0, "x: columns must be a multiple of 16")
+    _need(x.is_cuda, "x: must be on a GPU")
     dev = x.device
+    di = x.get_device()
     if out is None:
-        _on_gpu(dev, x)
         q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
         s = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
         g = torch.empty(1, dtype=torch.float32, device=dev)
+        res = Packed((q, s, g), _trusted=((), rows, cols, di))
     else:
-        q, s, g = out
-        _packed((q, s, g), rows, cols, "out")
+        res = _packed(tuple(out))
+        _need(not res.lead and res.rows == rows and res.K == cols and res.dev == di,
+              f"out: does not pack x [{rows}, {cols}] on its GPU")
+        q, s, g = res
     if global_scale is not None:
         _need(global_scale.dtype == torch.float32 and global_scale.numel() == 1,
               "global_scale: one fp32 value")
-        _on_gpu(dev, global_scale)
+        _on_dev(global_scale, di, "global_scale")
     if workspace is not None:
-        _on_gpu(dev, workspace)
-    _on_gpu(dev, x, q, s, g)
+        _on_dev(workspace, di, "workspace")
     flags = 0
     if global_scale is not None:
         g.copy_(global_scale.reshape(1))
@@ -200,27 +242,30 @@ def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None,
     st = nvfp4_quantize_raw(_ptr(x), _DT_IN[x.dtype], rows, cols, x.stride(0), _ptr(q), _ptr(s),
                             _ptr(g), flags, _ptr(workspace),
                             0 if workspace is None else workspace.numel() * workspace.element_size(),
-                            stream)
+                            _stream(stream, di))
     _check("nvfp4_quantize", st)
-    return q, s, g
+    return res
 
 
 def nvfp4_gemm(a, b, out_dtype: str = "bf16", y: torch.Tensor | None = None, stream=None):
     """a = (q, s, g) of x [M, K]; b = (q, s, g) of W [N, K] -> y [M, N]."""
+    if type(a) is not Packed:
+        a = Packed(a)
+    if type(b) is not Packed:
+        b = Packed(b)
+    if a.lead or b.lead or a.K != b.K or a.dev != b.dev:
+        raise ValueError("a and b: 2-D packed operands with the same K on one GPU")
     a_q, a_s, a_g = a
     b_q, b_s, b_g = b
-    _need(a_q.dim() == 2 and b_q.dim() == 2, "a and b: 2-D packed operands")
-    M, N, K = a_q.shape[0], b_q.shape[0], a_q.shape[1] * 2
-    _packed(a, M, K, "a")
-    _packed(b, N, K, "b")
+    M, N, K = a.rows, b.rows, a.K
     _need(out_dtype in _DT_OUT, f"out_dtype: one of {sorted(_DT_OUT)}")
     code, tdt = _DT_OUT[out_dtype]
     if y is None:
         y = torch.empty((M, N), dtype=tdt, device=a_q.device)
-    _out(y, M, N, tdt)
-    _on_gpu(a_q.device, a_q, a_s, a_g, b_q, b_s, b_g, y)
-    st = nvfp4_gemm_raw(M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s),
-                        _ptr(b_g), _ptr(y), code, y.stride(0), stream)
+    ld_y = _out(y, M, N, tdt, a.dev)
+    st = nvfp4_gemm_raw(M, N, K, a_q.data_ptr(), a_s.data_ptr(), a_g.data_ptr(), b_q.data_ptr(),
+                        b_s.data_ptr(), b_g.data_ptr(), y.data_ptr(), code, ld_y,
+                        _stream(stream, a.dev))
     _check("nvfp4_gemm", st)
     return y
 
@@ -229,22 +274,24 @@ def nvfp4_gemm_nvfp4_out(a, b, y_g: torch.Tensor, out=None, stream=None):
     """a = (q, s, g) of x [M, K], b = (q, s, g) of W [N, K]; y_g = the output's
     static global scale (fp32 [1], GPU) -> (q [M, N/2], s [M, N/16], y_g): y
     quantised in the GEMM's epilogue.  ``out`` = (q, s) reuses buffers."""
+    a, b = _packed(a), _packed(b)
+    _need(not a.lead and not b.lead and a.K == b.K and a.dev == b.dev,
+          "a and b: 2-D packed operands with the same K on one GPU")
     a_q, a_s, a_g = a
     b_q, b_s, b_g = b
-    _need(a_q.dim() == 2 and b_q.dim() == 2, "a and b: 2-D packed operands")
-    M, N, K = a_q.shape[0], b_q.shape[0], a_q.shape[1] * 2
-    _packed(a, M, K, "a")
-    _packed(b, N, K, "b")
+    M, N, K = a.rows, b.rows, a.K
     _need(N % 16 == 0, "the output's columns (rows of b) must be a multiple of 16")
     if out is None:
         q = torch.empty((M, N // 2), dtype=torch.uint8, device=a_q.device)
         s = torch.empty((M, N // 16), dtype=torch.uint8, device=a_q.device)
     else:
         q, s = out
-    _packed((q, s, y_g), M, N, "out")
-    _on_gpu(a_q.device, a_q, a_s, a_g, b_q, b_s, b_g, q, s, y_g)
+    o = Packed((q, s, y_g))
+    _need(not o.lead and o.rows == M and o.K == N and o.dev == a.dev,
+          f"out: must pack the output [{M}, {N}] on the operands' GPU")
     st = nvfp4_gemm_nvfp4_out_raw(M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q),
-                                  _ptr(b_s), _ptr(b_g), _ptr(q), _ptr(s), _ptr(y_g), stream)
+                                  _ptr(b_s), _ptr(b_g), _ptr(q), _ptr(s), _ptr(y_g),
+                                  _stream(stream, a.dev))
     _check("nvfp4_gemm_nvfp4_out", st)
     return q, s, y_g
 
@@ -256,33 +303,34 @@ def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: s
     b = (q [G, N, K/2], s [G, N, K/16], g [G]) -> y [total_m, N].
     With row_index (int32 [total_m], GPU), grouped row r reads row
     row_index[r] of a = (q [a_rows, K/2], s, g) instead (no gathered copy)."""
+    a, b = _packed(a), _packed(b)
+    _need(len(b.lead) == 1 and not a.lead and a.K == b.K and a.dev == b.dev,
+          "b: [G, N, K/2] packed experts and a: packed rows with the same K, on one GPU")
+    _need(row_index is not None or a.rows == total_m, "a: total_m rows (or give row_index)")
     a_q, a_s, a_g = a
     b_q, b_s, b_g = b
-    _need(b_q.dim() == 3 and a_q.dim() == 2, "b: [G, N, K/2] packed experts; a: 2-D packed rows")
-    G, N = b_q.shape[0], b_q.shape[1]
-    K = b_q.shape[2] * 2
-    _packed(b, N, K, "b", n_g=G)
-    _packed(a, a_q.shape[0] if row_index is not None else total_m, K, "a")
+    G, N, K = b.lead[0], b.rows, b.K
     _need(m_offsets.dtype == torch.int32 and m_offsets.numel() == G + 1
           and m_offsets.is_contiguous(), "m_offsets: G + 1 contiguous int32")
+    _on_dev(m_offsets, b.dev, "m_offsets")
     _need(out_dtype in _DT_OUT, f"out_dtype: one of {sorted(_DT_OUT)}")
     code, tdt = _DT_OUT[out_dtype]
     if y is None:
         y = torch.empty((total_m, N), dtype=tdt, device=b_q.device)
-    _out(y, total_m, N, tdt)
-    _on_gpu(b_q.device, a_q, a_s, a_g, b_q, b_s, b_g, m_offsets, y)
+    ld_y = _out(y, total_m, N, tdt, b.dev)
+    stream = _stream(stream, b.dev)
     if row_index is None:
         st = nvfp4_grouped_gemm_raw(G, _ptr(m_offsets), total_m, N, K, _ptr(a_q), _ptr(a_s),
                                     _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
-                                    y.stride(0), stream)
+                                    ld_y, stream)
         _check("nvfp4_grouped_gemm", st)
         return y
     _need(row_index.dtype == torch.int32 and row_index.numel() == total_m
           and row_index.is_contiguous(), "row_index: total_m contiguous int32")
-    _on_gpu(b_q.device, row_index)
+    _on_dev(row_index, b.dev, "row_index")
     st = nvfp4_grouped_gemm_gather_raw(G, _ptr(m_offsets), _ptr(row_index), total_m,
                                        a_q.shape[0], N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g),
                                        _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
-                                       y.stride(0), stream)
+                                       ld_y, stream)
     _check("nvfp4_grouped_gemm_gather", st)
     return y

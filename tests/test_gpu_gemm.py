@@ -379,3 +379,24 @@ def test_general_kernel_past_its_row_chunks():
     torch.cuda.synchronize()
     ref = oracle_quantize(torch.from_numpy(y_rows), np.float32(g.item()))
     assert_bytes_equal(q[idx], s[idx], g, *ref)
+
+
+def test_binding_checks_outputs_and_packs_operands():
+    """The quantiser returns checked Packed operands; an output buffer of the
+    wrong dtype, shape or layout is refused before the library is called."""
+    need_gpu()
+    x = wl.randn((8, 64), 8401, "bf16").cuda()
+    w = wl.randn((32, 64), 8402, "bf16").cuda()
+    a, b = nv.nvfp4_quantize(x), nv.nvfp4_quantize(w)
+    assert type(a) is nv.Packed and (a.rows, a.K) == (8, 64)
+    for y, dt in ((torch.empty((8, 32), dtype=torch.bfloat16, device="cuda"), "f32"),
+                  (torch.empty((8, 33), dtype=torch.float32, device="cuda"), "f32"),
+                  (torch.empty((32, 8), dtype=torch.float32, device="cuda").t(), "f32"),
+                  (torch.empty((8, 32), dtype=torch.float32), "f32")):
+        with pytest.raises(ValueError):
+            nv.nvfp4_gemm(a, b, dt, y=y)
+    with pytest.raises(ValueError):   # operands of different K
+        nv.nvfp4_gemm(a, nv.nvfp4_quantize(wl.randn((32, 128), 8403, "bf16").cuda()), "f32")
+    y = nv.nvfp4_gemm(tuple(a), tuple(b), "f32")     # plain tuples are checked and accepted
+    torch.cuda.synchronize()
+    assert y.shape == (8, 32)
