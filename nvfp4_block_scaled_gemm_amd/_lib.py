@@ -147,13 +147,13 @@ def _packed(t3) -> Packed:
 def _out(y, rows: int, cols: int, dtype, dev: int, what: str = "y") -> int:
     """Checks an output [rows, cols] of ``dtype`` on GPU ``dev``; returns its
     row stride."""
-    ld, cs = y.stride()
-    if y.dtype == dtype and y.shape == (rows, cols) and (cs == 1 or cols <= 1) \
+    st = y.stride()
+    if y.dtype == dtype and y.shape == (rows, cols) and (st[1] == 1 or cols <= 1) \
             and y.get_device() == dev:
-        return ld
+        return st[0]
     _need(y.dtype == dtype, f"{what}: dtype {y.dtype}, expected {dtype}")
     _need(y.shape == (rows, cols), f"{what}: shape {tuple(y.shape)}, expected ({rows}, {cols})")
-    _need(cs == 1 or cols <= 1, f"{what}: rows must have unit column stride")
+    _need(st[1] == 1 or cols <= 1, f"{what}: rows must have unit column stride")
     raise ValueError(f"{what}: must be on the operands' GPU")
 
 

@@ -245,3 +245,18 @@ def test_binding_rejects_mismatched_quantize_and_grouped_tensors():
         nv.nvfp4_grouped_gemm(torch.zeros(G + 1, dtype=torch.int32), total, a, (bq, bs, torch.ones(1)))
     with pytest.raises(ValueError):   # CPU tensors
         nv.nvfp4_grouped_gemm(torch.zeros(G + 1, dtype=torch.int32), total, a, b)
+
+
+def test_output_buffer_checks_on_host():
+    """The binding's output check (host tensors stand in for GPU buffers:
+    both report device -1 here)."""
+    import nvfp4_block_scaled_gemm_amd._lib as L
+    assert L._out(torch.empty((4, 8), dtype=torch.bfloat16), 4, 8, torch.bfloat16, -1) == 8
+    wide = torch.empty((4, 16), dtype=torch.bfloat16)[:, :8]        # row stride 16
+    assert L._out(wide, 4, 8, torch.bfloat16, -1) == 16
+    for bad in (torch.empty(32, dtype=torch.bfloat16), torch.empty((4, 8)),
+                torch.empty((8, 4), dtype=torch.bfloat16).t()):
+        with pytest.raises(ValueError):
+            L._out(bad, 4, 8, torch.bfloat16, -1)
+    with pytest.raises(ValueError):                                # another device
+        L._out(torch.empty((4, 8), dtype=torch.bfloat16), 4, 8, torch.bfloat16, 0)
