@@ -106,13 +106,16 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of x in the CPU oracle sample (4096 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy", "mfma_rate", "stream_rate"],
+    ap.add_argument("--mode", choices=["bench", "copy", "mfma_rate", "stream_rate",
+                                       "decode_sizes"],
                     default="bench",
                     help="copy: a plain 1 GiB device copy, for HBM counter calibration; "
                          "mfma_rate: the sustained fp16 MFMA rate alone and with 4 or 8 "
                          "dequantisation instructions per MFMA, on one CU and on all of them; "
                          "stream_rate: the grouped GEMM's weight-load pattern streaming "
-                         "gate_up-sized weights with nothing else running")
+                         "gate_up-sized weights with nothing else running; "
+                         "decode_sizes: the M = 1 decode GEMM against the weight size "
+                         "(K = 8192, N = 4096 .. 32768), cache-cold")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -206,6 +209,40 @@ def main():
             print(json.dumps({"mode": "stream_rate", "pattern": names[mode],
                               "busy_fmas_per_job": busy, "us": round(us, 1), "bytes": nbytes,
                               "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
+        return
+
+    if args.mode == "decode_sizes":
+        # per-launch fixed cost and streaming rate of the decode kernel: M = 1
+        # over rotating weight copies (at least 640 MB per rotation), 128
+        # launches back to back, median of three batches
+        stream = torch.cuda.current_stream()
+
+        def batch(fn, reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        kd = 8192
+        xd = nv.nvfp4_quantize(wl.randn((1, kd), wl.seed_for(2, 0), "bf16").to(dev))
+        for nd in (4096, 8192, 16384, 32768):
+            wq = nv.nvfp4_quantize(wl.randn((nd, kd), wl.seed_for(2, 1), "bf16").to(dev))
+            nbytes = nd * kd * 9 // 16
+            ncopy = max(2, (640 << 20) // nbytes)
+            copies = [nv.Packed(tuple(t.clone() for t in wq)) for _ in range(ncopy)]
+            yd = torch.empty((1, nd), dtype=torch.bfloat16, device=dev)
+            batch(lambda i: nv.nvfp4_gemm(xd, copies[i % ncopy], "bf16", y=yd), 128)
+            ms = sorted(batch(lambda i: nv.nvfp4_gemm(xd, copies[i % ncopy], "bf16", y=yd), 128)
+                        for _ in range(3))[1]
+            print(json.dumps({"mode": "decode_sizes", "M": 1, "N": nd, "K": kd,
+                              "weight_bytes": nbytes, "copies": ncopy,
+                              "us": round(ms * 1e3, 2)}), flush=True)
+            del copies, wq
+            torch.cuda.empty_cache()
         return
 
     cfg = wl.LINEAR
