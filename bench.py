@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+PREWARM_S = 1.0               # untimed back-to-back steps before timing
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_linear_m4096_n8192_k8192.json")
 GEMM_SOURCES = ["gemm_mfma.hip", "nvfp4_device.h"]
 
@@ -106,14 +107,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of x in the CPU oracle sample (4096 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy", "mfma_rate", "stream_rate",
-                                       "decode_sizes"],
+    ap.add_argument("--mode", choices=["bench", "copy", "decode_sizes"],
                     default="bench",
                     help="copy: a plain 1 GiB device copy, for HBM counter calibration; "
-                         "mfma_rate: the sustained fp16 MFMA rate alone and with 4 or 8 "
-                         "dequantisation instructions per MFMA, on one CU and on all of them; "
-                         "stream_rate: the grouped GEMM's weight-load pattern streaming "
-                         "gate_up-sized weights with nothing else running; "
                          "decode_sizes: the M = 1 decode GEMM against the weight size "
                          "(K = 8192, N = 4096 .. 32768), cache-cold")
     args = ap.parse_args()
@@ -135,80 +131,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read_per_copy": src.numel() * 4,
                           "bytes_written_per_copy": src.numel() * 4, "copies": args.steps}))
-        return
-
-    if args.mode == "mfma_rate":
-        import ctypes
-        probe = ctypes.CDLL(os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_probe.so"))
-        probe.probe_mfma_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
-        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        stream = torch.cuda.current_stream()
-        for blocks, iters in ((1, 20000), (n_cu, 100000)):
-            out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-            for nv_ops in (0, 4, 8):
-                def launch():
-                    rc = probe.probe_mfma_rate(nv_ops, blocks, 256, iters, out.data_ptr(),
-                                               ctypes.c_void_p(stream.cuda_stream))
-                    assert rc == 0, f"probe_mfma_rate returned {rc}"
-                # all-CU runs first hold the clock for ~30 ms while the power
-                # controller settles, so they warm up longer
-                for _ in range(6 if blocks > 1 else 1):
-                    launch()
-                torch.cuda.synchronize()
-                times = []
-                for _ in range(3):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    launch()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    times.append(e0.elapsed_time(e1) * 1e3)
-                us = sorted(times)[1]
-                ns_per_mfma = us * 1e3 / (4 * iters)          # one wave per SIMD
-                busy_cus = min(blocks, n_cu)
-                print(json.dumps({
-                    "mode": "mfma_rate", "workgroups": blocks, "busy_cus": busy_cus,
-                    "valu_per_mfma": nv_ops, "us": round(us, 1),
-                    "ns_per_mfma_per_simd": round(ns_per_mfma, 3),
-                    "tflops": round(busy_cus * 4 * 32768 / ns_per_mfma / 1e3, 1)}), flush=True)
-        return
-
-    if args.mode == "stream_rate":
-        import ctypes
-        probe = ctypes.CDLL(os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_probe.so"))
-        probe.probe_stream_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                            ctypes.c_void_p, ctypes.c_void_p]
-        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        stream = torch.cuda.current_stream()
-        n_items = 16384                                  # x 64 rows = 256 experts x 4096 rows
-        w = torch.full((n_items * 64 * 3072,), 0x11, dtype=torch.uint8, device=dev)
-        s = torch.full((n_items * 64 * 384,), 0x38, dtype=torch.uint8, device=dev)
-        out = torch.zeros(1, dtype=torch.int32, device=dev)
-        names = {0: "64 rows x 256 B jobs, nibbles only",
-                 1: "64 rows x 256 B jobs + scales 32 rows x 32 B per load (the grouped kernel)",
-                 2: "64 rows x 256 B jobs + scales by whole lines",
-                 3: "128 rows x 128 B jobs + scales 64 rows x 16 B per load"}
-        for mode, busy in ((0, 0), (1, 0), (2, 0), (3, 0), (1, 500), (1, 1000)):
-            ni = n_items // 2 if mode == 3 else n_items
-
-            def launch():
-                rc = probe.probe_stream_rate(mode, w.data_ptr(), s.data_ptr(), ni, busy, n_cu,
-                                             out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
-                assert rc == 0, f"probe_stream_rate returned {rc}"
-            for _ in range(5):
-                launch()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(10):
-                launch()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / 10
-            nbytes = w.numel() + (s.numel() if mode else 0)
-            print(json.dumps({"mode": "stream_rate", "pattern": names[mode],
-                              "busy_fmas_per_job": busy, "us": round(us, 1), "bytes": nbytes,
-                              "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
         return
 
     if args.mode == "decode_sizes":
@@ -260,6 +182,18 @@ def main():
         nv.nvfp4_quantize(x, out=xq, workspace=ws)
         nv.nvfp4_gemm(xq, wq, "bf16", y=y)
 
+    # Untimed pre-warm by time, whatever --warmup says: the clock takes tens
+    # of milliseconds to settle under a new all-CU load (the first launches
+    # after idle run ~25 % slower), so steps run back to back for at least
+    # PREWARM_S seconds before the --warmup steps and the timed region.
+    t_pre = time.perf_counter()
+    n_pre = 0
+    while time.perf_counter() - t_pre < PREWARM_S:
+        for _ in range(50):
+            step()
+        n_pre += 50
+        torch.cuda.synchronize()
+    prewarm_s = time.perf_counter() - t_pre
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -276,7 +210,9 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gemm_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    gemm_each = sorted(a.elapsed_time(b) for a, b in ev)
+    gemm_ms = sum(gemm_each) / args.steps
+    gemm_median_ms = gemm_each[len(gemm_each) // 2]
     ms_per_step = wall * 1e3 / args.steps
     flop = 2.0 * M * N * K
     value = flop / (ms_per_step * 1e-3) / 1e12
@@ -429,28 +365,6 @@ def main():
                          "tflops": round(2.0 * tot_ * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
         del bq, bs, bg, a, ym, experts, a_op
 
-    # Same-box reference for the dense GEMM: the sustained rate of pure fp16
-    # MFMAs on every CU (the probe of --mode mfma_rate, no memory traffic,
-    # clock settled), and the GEMM's fraction of it.  Context only: the
-    # roofline above keeps the data-sheet peak.
-    probe_ref = None
-    try:
-        import ctypes
-        probe = ctypes.CDLL(os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_probe.so"))
-        probe.probe_mfma_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
-        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        pout = torch.empty(n_cu * 256, dtype=torch.float32, device=dev)
-        iters = 100000
-        launch = lambda i: probe.probe_mfma_rate(0, n_cu, 256, iters, pout.data_ptr(),  # noqa: E731
-                                                 ctypes.c_void_p(stream.cuda_stream))
-        timed(launch, 6)
-        pms = sorted(timed(launch, 1) for _ in range(3))[1]
-        ptf = n_cu * 4 * 4 * iters * 32768 / (pms * 1e-3) / 1e12
-        probe_ref = {"pure_fp16_mfma_tflops_all_cus": round(ptf, 1),
-                     "gemm_frac_of_it": round(gemm_tflops / ptf, 4)}
-    except OSError:
-        pass
-
     # Large outlier workload M = N = K = 16384 (1 % of entries x50): the
     # quantiser on x timed alone (two reads of x + the packed writes), then
     # the GEMM.  Inputs are drawn on the GPU (same recipe, CUDA generator).
@@ -515,6 +429,8 @@ def main():
                    "step": "quantize x (amax+encode) + nvfp4_gemm; W quantized ahead"},
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_us": round(gemm_ms * 1e3, 2),
+        "gemm_us_median": round(gemm_median_ms * 1e3, 2),
+        "prewarm": {"seconds": round(prewarm_s, 3), "steps": n_pre},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4),
@@ -524,7 +440,6 @@ def main():
         "moe_grouped": dict(moe, peak_GBps=PEAK_HBM_GBS),
         "large": large,
         "fused_quant_out": fused,
-        "mfma_sustained_probe": probe_ref,
         "mid_m": dict(mid_m, workload="m{64..1024}_n8192_k8192, 16 rotating weight copies"),
         "library_reference": library,
     }

@@ -7,6 +7,7 @@ there is no fallback implementation.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -93,6 +94,18 @@ def _stream(stream=None, dev: int | None = None):
     if _raw_stream is not None:
         return _raw_stream(dev)
     return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _on_stream(stream, dev: int):
+    """Context in which the wrapper's own torch work (output allocations, the
+    static-scale copy, its internal workspace) is ordered on the same stream
+    as the library call: ``stream`` when given (a torch stream or a raw
+    handle), else nothing to change (the current stream is used by both)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream, device=dev)
+    return torch.cuda.stream(stream)
 
 
 _DT_IN = {torch.float32: NVFP4_F32, torch.bfloat16: NVFP4_BF16}
@@ -214,6 +227,12 @@ def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None,
     rows, cols = x.shape
     _need(cols % 16 == 0, "x: columns must be a multiple of 16")
     _need(x.is_cuda, "x: must be on a GPU")
+    with _on_stream(stream, x.get_device()):
+        return _quantize(x, global_scale, out, workspace)
+
+
+def _quantize(x, global_scale, out, workspace):
+    rows, cols = x.shape
     dev = x.device
     di = x.get_device()
     if out is None:
@@ -242,7 +261,7 @@ def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None,
     st = nvfp4_quantize_raw(_ptr(x), _DT_IN[x.dtype], rows, cols, x.stride(0), _ptr(q), _ptr(s),
                             _ptr(g), flags, _ptr(workspace),
                             0 if workspace is None else workspace.numel() * workspace.element_size(),
-                            _stream(stream, di))
+                            _stream(None, di))
     _check("nvfp4_quantize", st)
     return res
 
@@ -261,7 +280,8 @@ def nvfp4_gemm(a, b, out_dtype: str = "bf16", y: torch.Tensor | None = None, str
     _need(out_dtype in _DT_OUT, f"out_dtype: one of {sorted(_DT_OUT)}")
     code, tdt = _DT_OUT[out_dtype]
     if y is None:
-        y = torch.empty((M, N), dtype=tdt, device=a_q.device)
+        with _on_stream(stream, a.dev):
+            y = torch.empty((M, N), dtype=tdt, device=a_q.device)
     ld_y = _out(y, M, N, tdt, a.dev)
     st = nvfp4_gemm_raw(M, N, K, a_q.data_ptr(), a_s.data_ptr(), a_g.data_ptr(), b_q.data_ptr(),
                         b_s.data_ptr(), b_g.data_ptr(), y.data_ptr(), code, ld_y,
@@ -282,8 +302,9 @@ def nvfp4_gemm_nvfp4_out(a, b, y_g: torch.Tensor, out=None, stream=None):
     M, N, K = a.rows, b.rows, a.K
     _need(N % 16 == 0, "the output's columns (rows of b) must be a multiple of 16")
     if out is None:
-        q = torch.empty((M, N // 2), dtype=torch.uint8, device=a_q.device)
-        s = torch.empty((M, N // 16), dtype=torch.uint8, device=a_q.device)
+        with _on_stream(stream, a.dev):
+            q = torch.empty((M, N // 2), dtype=torch.uint8, device=a_q.device)
+            s = torch.empty((M, N // 16), dtype=torch.uint8, device=a_q.device)
     else:
         q, s = out
     o = Packed((q, s, y_g))
@@ -316,7 +337,8 @@ def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: s
     _need(out_dtype in _DT_OUT, f"out_dtype: one of {sorted(_DT_OUT)}")
     code, tdt = _DT_OUT[out_dtype]
     if y is None:
-        y = torch.empty((total_m, N), dtype=tdt, device=b_q.device)
+        with _on_stream(stream, b.dev):
+            y = torch.empty((total_m, N), dtype=tdt, device=b_q.device)
     ld_y = _out(y, total_m, N, tdt, b.dev)
     stream = _stream(stream, b.dev)
     if row_index is None:

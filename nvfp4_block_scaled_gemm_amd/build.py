@@ -3,9 +3,7 @@
     python -m nvfp4_block_scaled_gemm_amd.build
 
 Every source compiles to an object under ``_build/`` (in parallel), then one
-shared library is linked next to this file.  Always rebuilds.  The
-measurement probes under ``probe/`` (used only by ``bench.py``'s probe modes)
-link into a library of their own, ``libnvfp4_probe.so``.
+shared library is linked next to this file.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -21,8 +19,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
-PROBE_SRC = os.path.join(PKG, "probe")
-PROBE_LIB = os.path.join(PKG, "libnvfp4_probe.so")
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of generated code (the device compile
@@ -44,14 +40,8 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def probe_sources():
-    return sorted(os.path.join(PROBE_SRC, f) for f in os.listdir(PROBE_SRC)
-                  if f.endswith(".hip"))
-
-
 def _compile(src: str) -> str:
-    sub = "probe_" if os.path.dirname(src) == PROBE_SRC else ""
-    obj = os.path.join(BUILD, sub + os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -79,14 +69,12 @@ def _link(objs, lib: str) -> None:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs, psrcs = sources(), probe_sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
-        objs = list(ex.map(_compile, srcs + psrcs))
-    _link(objs[:len(srcs)], LIB)
-    _link(objs[len(srcs):], PROBE_LIB)
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs, LIB)
     if verbose:
         print(f"built {LIB}")
-        print(f"built {PROBE_LIB}")
     return LIB
 
 

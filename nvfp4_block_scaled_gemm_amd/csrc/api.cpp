@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "nvfp4_dispatch.h"
 #include "nvfp4_internal.h"
 
 namespace {
@@ -27,8 +28,11 @@ bool tiled_ok(int64_t K, const uint8_t* q, const uint8_t* s, int64_t kmult) {
   return K % kmult == 0 && aligned(q, 16) && aligned(s, 8);
 }
 
-// The MFMA tile kernel addresses each operand with 32-bit byte offsets.
-bool offsets32_ok(int64_t rows, int64_t K) { return (rows + 32) * (K / 2) < ((int64_t)1 << 32) - 16; }
+using nvfp4::offsets32_ok;
+
+nvfp4::OperandAlign align_of(const uint8_t* q, const uint8_t* s) {
+  return {aligned(q, 16), aligned(s, 8), aligned(s, 16)};
+}
 
 // Shared body of the two grouped entry points (row_index == nullptr: rows
 // of A are the grouped rows themselves, a_rows == total_m).
@@ -61,19 +65,18 @@ int gemm_dispatch(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uin
                   const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
                   void* y, int dt, int64_t ld_y, nvfp4::QuantOut qo, hipStream_t st) {
   const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
-  // K == 0: the sum is empty; the general kernel writes zeros.  97-128 rows
-  // go to the MFMA kernel's 64 x 64 tiles when those fill the chip (one
-  // pass over W, ~38 us at N = K = 8192 whatever M), else to the decode
-  // kernel's two 64-row passes, whose second pass costs less the fewer
-  // rows it has (34 / 39 / 47 us at M = 65 / 96 / 128).
-  const bool mid_mfma = M > 96 && ((M + 63) / 64) * ((N + 63) / 64) >= 256;
-  if (K > 0 && M <= 128 && !mid_mfma && tiled_ok(K, a_q, a_s, 256) &&
-      tiled_ok(K, b_q, b_s, 256) && offsets32_ok(N, K))
-    return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st, qo));
-  if (K > 0 && tiled_ok(K, a_q, a_s, 128) && tiled_ok(K, b_q, b_s, 128) &&
-      offsets32_ok(M, K) && offsets32_ok(N, K))
-    return from_hip(nvfp4::launch_gemm_mfma(M, N, K, a, b, y, dt, ld_y, st, qo));
-  return from_hip(nvfp4::launch_gemm_generic(M, N, K, a, b, y, dt, ld_y, st, qo));
+  switch (nvfp4::gemm_path(M, N, K, align_of(a_q, a_s), align_of(b_q, b_s), dt == 2)) {
+    case nvfp4::GemmPath::kDecodeRows:
+      return from_hip(nvfp4::launch_gemm_decode_rows(M, N, K, a, b, y, dt, ld_y, st));
+    case nvfp4::GemmPath::kDecodeLds:
+      return from_hip(nvfp4::launch_gemm_decode_lds(M, N, K, a, b, y, dt, ld_y, st, qo));
+    case nvfp4::GemmPath::kDecode:
+      return from_hip(nvfp4::launch_gemm_decode(M, N, K, a, b, y, dt, ld_y, st, qo));
+    case nvfp4::GemmPath::kMfma:
+      return from_hip(nvfp4::launch_gemm_mfma(M, N, K, a, b, y, dt, ld_y, st, qo));
+    default:
+      return from_hip(nvfp4::launch_gemm_generic(M, N, K, a, b, y, dt, ld_y, st, qo));
+  }
 }
 
 }  // namespace

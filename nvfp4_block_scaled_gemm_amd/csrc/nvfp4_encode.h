@@ -210,8 +210,8 @@ __device__ __forceinline__ void encode_exact(const Block16& b, int c, const Enco
 
 // Encodes one block (16 values in b) to its 8 nibble bytes and scale byte.
 //   kMode 0: g == 0 (every scale code 0, magnitudes 0)
-//   kMode 1: g >= 2^-88 (fast path below)
-//   kMode 2: 0 < g < 2^-88 (exact thresholds through fp64 throughout)
+//   kMode 1: 2^-88 <= g < 2^116 (fast path below)
+//   kMode 2: any other g > 0 (exact thresholds through fp64 throughout)
 template <int kMode>
 __device__ __forceinline__ void encode_block(const Block16& b, const EncodeParams& P,
                                              uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
@@ -306,10 +306,15 @@ __device__ __forceinline__ EncodeParams make_params(float g) {
   return P;
 }
 
-// encode_block's mode for global scale g: 0 for g == 0, 1 for g >= 2^-88,
-// 2 for the tiny scales in between.
+// encode_block's mode for global scale g: 0 for g == 0; 1 for
+// 2^-88 <= g < 2^116; 2 (exact fp64 thresholds) for the scales outside.
+// The fast mode needs fl32(1 / 6g) and fl32(1 / (E4M3(s) g)) to be normal
+// fp32 numbers, so that their relative error stays far inside the 2^-20
+// half-width of its intervals: E4M3(s) <= 448 < 2^9, so g < 2^116 keeps
+// E4M3(s) g below 2^125 and 6g below 2^119; below 2^-88 the residual
+// products underflow instead.
 __device__ __forceinline__ int encode_mode(float g) {
-  return !(g > 0.0f) ? 0 : (g >= 0x1p-88f ? 1 : 2);
+  return !(g > 0.0f) ? 0 : ((g >= 0x1p-88f && g < 0x1p116f) ? 1 : 2);
 }
 
 }  // namespace enc

@@ -48,6 +48,19 @@ hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a,
                             PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                             hipStream_t stream, QuantOut qo = {});
 
+// gemm_decode_lds.hip: M <= 32, K % 1024 == 0, 16-byte aligned nibble and
+// scale bases, both operands' bytes < 4 GiB.
+hipError_t launch_gemm_decode_lds(int64_t M, int64_t N, int64_t K, PackedOperand a,
+                                  PackedOperand b, void* y, int y_dtype, int64_t ld_y,
+                                  hipStream_t stream, QuantOut qo = {});
+
+// gemm_decode_rows.hip: whole-row weight stream for the shapes
+// decode_rows_shape (nvfp4_dispatch.h) accepts, fp32 / bf16 output only;
+// 16-byte aligned nibble and scale bases, both operands' bytes < 4 GiB.
+hipError_t launch_gemm_decode_rows(int64_t M, int64_t N, int64_t K, PackedOperand a,
+                                   PackedOperand b, void* y, int y_dtype, int64_t ld_y,
+                                   hipStream_t stream);
+
 // gemm_skinny.hip: M <= 128 (decode; 64-row passes), K % 256 == 0, N * K / 2 < 4 GiB.
 hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a,
                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,

@@ -27,7 +27,7 @@
 // interval around the quotient; where the ends disagree a midpoint lies in
 // the interval and an exact test settles the code (an fp64 midpoint search
 // for the scale, an fma residual sign for an element).  Tensors with
-// g < 2^-88 take exact fp64 threshold comparisons throughout.
+// g < 2^-88 or g >= 2^116 take exact fp64 threshold comparisons throughout.
 #include "nvfp4_device.h"
 #include "nvfp4_encode.h"
 #include "nvfp4_internal.h"

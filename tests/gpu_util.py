@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import nvfp4_block_scaled_gemm_amd as nv
-from oracle import quantize_ref
+from oracle import global_scale_ref, quantize_ref
 
 
 def need_gpu():
@@ -35,8 +35,8 @@ def oracle_quantize(x_cpu: torch.Tensor, global_scale=None):
 
 
 def oracle_global_scale(x_cpu: torch.Tensor) -> np.float32:
-    amax = np.float32(x_cpu.abs().max().float().item()) if x_cpu.numel() else np.float32(0)
-    return np.float32(amax / np.float32(2688.0))
+    """The oracle's global scale of a whole CPU tensor (bf16 widens exactly)."""
+    return global_scale_ref(np_(x_cpu))
 
 
 def to_gpu(q, s, g):

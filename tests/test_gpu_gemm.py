@@ -195,9 +195,11 @@ def test_bf16_output_is_rne_of_f32_and_repeatable():
         assert torch.equal(_gemm(a, b, "f32"), y32)
 
 
-def test_linear_workload_sampled():
-    """M=4096, N=K=8192 bf16 inputs quantised on the GPU (bytes checked on the
-    sampled rows), GEMM in bf16 checked on a 256 x 256 sample of outputs."""
+def test_linear_workload_full():
+    """M=4096, N=K=8192 bf16 inputs quantised on the GPU, every byte and both
+    global scales checked against the oracle; the whole bf16 output of the
+    GEMM (the launch configuration the bench times) against the fp64 oracle
+    GEMM."""
     need_gpu()
     x_cpu, w_cpu = wl.gemm_inputs(1, wl.LINEAR)
     note("linear workload quantize")
@@ -205,38 +207,29 @@ def test_linear_workload_sampled():
     b = nv.nvfp4_quantize(w_cpu.cuda())
     note("linear workload gemm")
     y = _gemm(a, b, "bf16")
-    rng = np.random.default_rng(11)
-    rows = np.sort(rng.choice(wl.LINEAR.M, 256, replace=False))
-    cols = np.sort(rng.choice(wl.LINEAR.N, 256, replace=False))
-    ra = oracle_quantize(x_cpu[torch.from_numpy(rows)], oracle_global_scale(x_cpu))
-    rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
-    assert_bytes_equal(*a, *ra, rows=rows)
-    assert_bytes_equal(*b, *rb, rows=cols)
-    y_ref, bound = gemm_ref(*ra, *rb)
-    ok, worst = check_gemm(np_(y)[np.ix_(rows, cols)], y_ref, bound, "bf16")
-    assert ok, worst
-
-
-@pytest.mark.parametrize("M", [1, 16, 32])
-def test_decode_workload(M):
-    need_gpu()
-    cfg = wl.DECODE[M]
-    x_cpu, w_cpu = wl.gemm_inputs(2, cfg)
-    a = nv.nvfp4_quantize(x_cpu.cuda())
-    b = nv.nvfp4_quantize(w_cpu.cuda())
-    note(f"decode M={M}")
-    y = _gemm(a, b, "bf16")
-    cols = np.sort(np.random.default_rng(M).choice(cfg.N, 1024, replace=False))
+    note("linear workload: oracle quantise of x and W")
     ra = oracle_quantize(x_cpu)
-    rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
+    rb = oracle_quantize(w_cpu)
     assert_bytes_equal(*a, *ra)
-    assert_bytes_equal(*b, *rb, rows=cols)
+    assert_bytes_equal(*b, *rb)
+    note("linear workload: oracle GEMM (fp64, full output)")
     y_ref, bound = gemm_ref(*ra, *rb)
-    ok, worst = check_gemm(np_(y)[:, cols], y_ref, bound, "bf16")
+    ok, worst = check_gemm(np_(y), y_ref, bound, "bf16")
     assert ok, worst
 
 
-def test_large_outlier_workload_sampled():
+def _rows_of(packed, rows):
+    q, s, g = packed
+    idx = torch.from_numpy(np.asarray(rows)).to(q.device)
+    return np_(q.index_select(0, idx)), np_(s.index_select(0, idx))
+
+
+def test_large_outlier_workload():
+    """M = N = K = 16384 with 1 % x50 outliers, quantised on the GPU.  The
+    oracle quantises all of x and W (row chunks; global scales from the whole
+    tensors) and every byte must match.  The bf16 GEMM output is checked in
+    full over K on 64 random rows, 64 random columns and 4096 random
+    elements."""
     need_gpu()
     c = wl.LARGE
     x_cpu, w_cpu = wl.gemm_inputs(4, c)
@@ -245,16 +238,45 @@ def test_large_outlier_workload_sampled():
     b = nv.nvfp4_quantize(w_cpu.cuda())
     note("large workload gemm")
     y = _gemm(a, b, "bf16")
+    ref = {}
+    for name, t_cpu, got in (("x", x_cpu, a), ("W", w_cpu, b)):
+        g = oracle_global_scale(t_cpu)
+        assert np.float32(np_(got[2])[0]) == g, name
+        qs, ss = [], []
+        for r0 in range(0, t_cpu.shape[0], 2048):
+            note(f"large workload: oracle quantise of {name} rows {r0}..{r0 + 2047}")
+            rq, rs, _ = oracle_quantize(t_cpu[r0:r0 + 2048], g)
+            gq, gs = _rows_of(got, range(r0, min(r0 + 2048, t_cpu.shape[0])))
+            assert np.array_equal(gq, rq) and np.array_equal(gs, rs), (name, r0)
+            qs.append(rq)
+            ss.append(rs)
+        ref[name] = (np.concatenate(qs), np.concatenate(ss), g)
+    rq_x, rs_x, gx = ref["x"]
+    rq_w, rs_w, gw = ref["W"]
     rng = np.random.default_rng(4)
     rows = np.sort(rng.choice(c.M, 64, replace=False))
-    cols = np.sort(rng.choice(c.N, 128, replace=False))
-    ra = oracle_quantize(x_cpu[torch.from_numpy(rows)], oracle_global_scale(x_cpu))
-    rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
-    assert_bytes_equal(*a, *ra, rows=rows)
-    assert_bytes_equal(*b, *rb, rows=cols)
-    y_ref, bound = gemm_ref(*ra, *rb)
-    ok, worst = check_gemm(np_(y)[np.ix_(rows, cols)], y_ref, bound, "bf16")
-    assert ok, worst
+    cols = np.sort(rng.choice(c.N, 64, replace=False))
+    y_np = np_(y)
+    note("large workload: oracle GEMM on 64 full rows")
+    y_ref, bound = gemm_ref(rq_x[rows], rs_x[rows], gx, rq_w, rs_w, gw)
+    ok, worst = check_gemm(y_np[rows], y_ref, bound, "bf16")
+    assert ok, ("rows", worst)
+    note("large workload: oracle GEMM on 64 full columns")
+    y_ref, bound = gemm_ref(rq_x, rs_x, gx, rq_w[cols], rs_w[cols], gw)
+    ok, worst = check_gemm(y_np[:, cols], y_ref, bound, "bf16")
+    assert ok, ("cols", worst)
+    note("large workload: oracle GEMM on 4096 random elements")
+    em = rng.integers(0, c.M, 4096)
+    en = rng.integers(0, c.N, 4096)
+    for i0 in range(0, 4096, 512):
+        m, n = em[i0:i0 + 512], en[i0:i0 + 512]
+        xa = dequantize_ref(rq_x[m], rs_x[m])
+        wb = dequantize_ref(rq_w[n], rs_w[n])
+        alpha = float(np.float64(gx) * np.float64(gw))
+        y_ref = np.einsum("ik,ik->i", xa, wb) * alpha
+        bound = np.einsum("ik,ik->i", np.abs(xa), np.abs(wb)) * abs(alpha)
+        ok, worst = check_gemm(y_np[m, n], y_ref, bound, "bf16")
+        assert ok, ("elements", i0, worst)
 
 
 @pytest.mark.parametrize("out,pad,shift", [("bf16", 8, 0), ("bf16", 3, 0), ("bf16", 8, 1),

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import nvfp4_block_scaled_gemm_amd as nv
-from oracle import check_gemm, gemm_ref, quantize_ref
+from oracle import check_gemm, gemm_ref, pack_nibbles, quantize_ref
 from tests.gpu_util import need_gpu, note, np_, to_gpu
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +89,75 @@ def test_fused_output_zero_and_tiny_scales(M, N, K):
     (the encoder's exact-threshold mode; everything saturates)."""
     _fused_case(M, N, K, lambda y: np.float32(0.0), seed=M, check_fp32=False)
     _fused_case(M, N, K, lambda y: np.float32(2.0 ** -100), seed=M + 1, check_fp32=False)
+
+
+def _e4m3(c):
+    e, m = c >> 3, c & 7
+    return m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+
+
+# E2M1 midpoint m (between two magnitudes) written as hi + lo / 2 with hi, lo
+# E2M1 magnitudes, so that m * v = hi * v + lo * (v / 2) for an E4M3 value v
+_MID_SPLIT = {0.25: (0.0, 0.5), 0.75: (0.5, 0.5), 1.25: (1.0, 0.5), 1.75: (1.5, 0.5),
+              2.5: (2.0, 1.0), 3.5: (3.0, 1.0), 5.0: (4.0, 2.0)}
+_E2M1_CODE = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+
+
+def _midpoint_operands(M, K):
+    """A: M identical rows, nibble 1.0 at K-positions 0 and 16 (blocks 0 and
+    1, scale 1.0, g = 1), so y[:, n] = gb * (W[n, 0] + W[n, 16]).  W has 16
+    rows per output block j.  Row 16j holds 3.0 x E4M3(k) at position 0 and
+    3.0 x E4M3(k + 1) at 16: y = gb * 6 * (the midpoint between codes k and
+    k + 1), so under y_g = gb the block's scale quotient is that midpoint
+    exactly.  Rows 16j + 1 .. 7 sum to each E2M1 midpoint times E4M3(c), c
+    the even one of k, k + 1 (the block's scale code), rows + 8 .. 14 the
+    same negated, row 16j + 15 zero."""
+    ks = list(range(16, 98))                 # 6 * 2^120 * the midpoint stays finite
+    N = 16 * len(ks)
+    nib = np.zeros((N, K), np.uint8)
+    sc = np.full((N, K // 16), 0x38, np.uint8)
+    for j, k in enumerate(ks):
+        r = 16 * j
+        nib[r, 0], nib[r, 16] = 0x5, 0x5
+        sc[r, 0], sc[r, 1] = k, k + 1
+        c = k if k % 2 == 0 else k + 1
+        for i, m in enumerate(sorted(_MID_SPLIT)):
+            hi, lo = _MID_SPLIT[m]
+            assert hi * _e4m3(c) + lo * _e4m3(c - 8) == m * _e4m3(c)
+            for sign, rr in ((0, r + 1 + i), (8, r + 8 + i)):
+                nib[rr, 0] = sign | _E2M1_CODE[hi]
+                nib[rr, 16] = sign | _E2M1_CODE[lo]
+                sc[rr, 0], sc[rr, 1] = c, c - 8
+    a_nib = np.zeros((M, K), np.uint8)
+    a_nib[:, 0] = 0x2
+    a_nib[:, 16] = 0x2
+    a = (pack_nibbles(a_nib), np.full((M, K // 16), 0x38, np.uint8), np.float32(1))
+    b = (pack_nibbles(nib), sc, np.float32(2.0 ** 120))
+    return a, b
+
+
+@pytest.mark.parametrize("M,K", [(4, 1024), (40, 256), (256, 128), (4, 48)])
+def test_large_output_scale_on_midpoints(M, K):
+    """y_g = 2^120 and its fp32 neighbours (the exact-threshold encoder mode):
+    outputs exactly on E4M3 scale midpoints and E2M1 element midpoints (and,
+    with the neighbouring scales, one ulp of the quotient either side),
+    through each kernel of the dispatch (decode through LDS, decode in
+    64-row passes, MFMA tiles, general).  Bytes equal the oracle's encoding
+    of the fp32 output."""
+    need_gpu()
+    a, b = _midpoint_operands(M, K)
+    ga, gb = to_gpu(*a), to_gpu(*b)
+    note(f"gemm nvfp4 out on midpoints M={M} K={K}")
+    y32 = nv.nvfp4_gemm(ga, gb, out_dtype="f32")
+    torch.cuda.synchronize()
+    y_np = np_(y32)
+    y_ref, bound = gemm_ref(*a, *b)
+    assert np.array_equal(y_np.astype(np.float64), y_ref)      # every output exact
+    g0 = np.float32(2.0 ** 120)
+    for g in (g0, np.nextafter(g0, np.float32(np.inf)), np.nextafter(g0, np.float32(0))):
+        yg = torch.tensor([float(g)], dtype=torch.float32, device="cuda")
+        q, s, _ = nv.nvfp4_gemm_nvfp4_out(ga, gb, yg)
+        torch.cuda.synchronize()
+        rq, rs, _ = quantize_ref(y_np, global_scale=g)
+        assert np.array_equal(np_(s), rs), f"scale bytes differ (g = {g})"
+        assert np.array_equal(np_(q), rq), f"packed bytes differ (g = {g})"

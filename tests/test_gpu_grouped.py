@@ -5,7 +5,7 @@ import torch
 
 import nvfp4_block_scaled_gemm_amd as nv
 import workloads as wl
-from oracle import check_gemm, gemm_ref, grouped_gemm_ref, pack_nibbles
+from oracle import check_gemm, gemm_ref, global_scale_ref, grouped_gemm_ref, pack_nibbles
 from tests.gpu_util import (assert_bytes_equal, need_gpu, note, np_, oracle_global_scale,
                             oracle_quantize)
 
@@ -171,17 +171,27 @@ def _moe_case(proj: str, gather: bool = False):
                               row_index=row_index)
     torch.cuda.synchronize()
     y_np = np_(y)
-    ga = oracle_global_scale(x_cpu)
-    cols = np.sort(np.random.default_rng(7).choice(N, 256, replace=False))
+    note(f"moe {proj}: oracle quantise of the activations")
+    ra_all = oracle_quantize(x_cpu)
+    assert_bytes_equal(q if proj == "gate_up" else a[0], s if proj == "gate_up" else a[1],
+                       g if proj == "gate_up" else a[2], *ra_all)
     off = routing.m_offsets.numpy()
-    for e in (0, 97, 255):
+    rng = np.random.default_rng(7)
+    note(f"moe {proj}: every expert with rows, 64 sampled output columns each")
+    for e in range(E):
         r0, r1 = int(off[e]), int(off[e + 1])
-        assert r1 > r0
-        w_cpu = wl.randn((N, K), wseed(e), "bf16", device=dev).cpu()
-        rb = oracle_quantize(w_cpu[torch.from_numpy(cols)], oracle_global_scale(w_cpu))
+        if r1 == r0:
+            continue
+        cols = np.sort(rng.choice(N, 64, replace=False))
+        w = wl.randn((N, K), wseed(e), "bf16", device=dev)
+        # the expert's amax is an exact, order-free reduction (taken on the
+        # device); the oracle turns it into the global scale
+        gw = global_scale_ref(np.array([w.abs().max().float().item()], np.float32))
+        w_cols = w.index_select(0, torch.from_numpy(cols).to(dev)).cpu()
+        rb = oracle_quantize(w_cols, gw)
         assert_bytes_equal(bq[e], bs[e], bg[e:e + 1], *rb, rows=cols)
-        ra = oracle_quantize(x_cpu[rows_tok[r0:r1]], ga)
-        y_ref, bound = gemm_ref(*ra, *rb)
+        rows = rows_tok[r0:r1].numpy()
+        y_ref, bound = gemm_ref(ra_all[0][rows], ra_all[1][rows], ra_all[2], *rb)
         ok, worst = check_gemm(y_np[r0:r1][:, cols], y_ref, bound, "bf16")
         assert ok, (e, worst)
 

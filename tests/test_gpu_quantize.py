@@ -157,3 +157,62 @@ def test_repeat_is_bitwise_identical():
     b = nv.nvfp4_quantize(x)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+_BIG = float(np.float32(2.0 ** 116))
+_LARGE_G = [2.0 ** 120, 1e37, 3e38, _BIG, float(np.nextafter(np.float32(_BIG), np.float32(0)))]
+
+
+@pytest.mark.parametrize("g", _LARGE_G)
+def test_large_static_scale_scale_code_ties(g):
+    """Static global scales at and above 2^116, where 1 / 6g and
+    1 / (E4M3(s) g) leave the normal fp32 range: block maxima on every E4M3
+    midpoint times 6g that fp32 can hold, and one fp32 step either side."""
+    v = _e4m3_values()
+    mids = (v[:-1] + v[1:]) / 2 * 6 * np.float64(np.float32(g))
+    mids = mids[mids < np.finfo(np.float32).max / 2]
+    m32 = mids.astype(np.float32)
+    vals = np.concatenate([m32, np.nextafter(m32, np.float32(np.inf)),
+                           np.nextafter(m32, np.float32(0))])
+    vals = vals[np.isfinite(vals) & (vals > 0)]
+    x = np.zeros((len(vals), 16), dtype=np.float32)
+    x[:, 5] = vals
+    x[:, 9] = -vals / 3
+    x[:, 12] = vals / 7
+    _check(torch.from_numpy(x), global_scale=g)
+
+
+@pytest.mark.parametrize("g", _LARGE_G)
+def test_large_static_scale_element_thresholds(g):
+    """For every scale code whose block fits fp32 under static scale g: a
+    block maximum of 6 E4M3(c) g and elements on each E2M1 midpoint times
+    E4M3(c) g, and one fp32 step either side."""
+    v = _e4m3_values()
+    gd = np.float64(np.float32(g))
+    mid2 = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    rows = []
+    for c in range(1, 127):
+        S = v[c] * gd
+        if 6 * S >= np.finfo(np.float32).max / 2:
+            break
+        for side in (0, 1, 2):
+            blk = np.zeros(16, np.float32)
+            blk[0] = np.float32(6 * S)
+            t = (mid2 * S).astype(np.float32)
+            if side == 1:
+                t = np.nextafter(t, np.float32(np.inf))
+            elif side == 2:
+                t = np.nextafter(t, np.float32(0))
+            blk[1:8] = t
+            blk[8:15] = -t
+            rows.append(blk)
+    _check(torch.from_numpy(np.stack(rows)), global_scale=g)
+
+
+@pytest.mark.parametrize("g", [1e37, 3e38])
+def test_large_static_scale_random(g):
+    """Random data, outliers included, under huge static scales (most scale
+    codes subnormal or zero)."""
+    x = wl.randn((64, 512), 41, "fp32", True) * 1e36
+    _check(x, global_scale=g)
+    _check(x.to(torch.bfloat16), global_scale=g)

@@ -95,3 +95,39 @@ def test_graph_capture_and_replay():
         torch.cuda.synchronize()
         for r, got in zip(ref, _snapshot(b)):
             assert torch.equal(r, got), f"replay {rep} differs"
+
+
+def test_side_stream_without_context_static_scale():
+    """stream=side with torch's current stream left as it is: the wrapper's
+    own torch work (the static scale copied into g, freshly allocated
+    outputs) must be ordered on the side stream too.  The current stream is
+    kept busy meanwhile, so work left on it would land after the kernels
+    that need it."""
+    need_gpu()
+    dev = "cuda"
+    x = wl.randn((256, 1024), 21, "bf16").to(dev)
+    w = wl.randn((384, 1024), 22, "bf16").to(dev)
+    gs = torch.tensor([0.0029], dtype=torch.float32, device=dev)
+    ref_x = nv.nvfp4_quantize(x, global_scale=gs)
+    wq = nv.nvfp4_quantize(w)
+    ref_y = nv.nvfp4_gemm(ref_x, wq, "f32")
+    ref_o = nv.nvfp4_gemm_nvfp4_out(ref_x, wq, gs)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    note("entry points with stream=side, current stream busy")
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(100_000_000)          # ~50 ms of spinning on the current stream
+    else:  # pragma: no cover
+        big = torch.randn((4096, 4096), device=dev)
+        for _ in range(20):
+            big = big @ big.t() * 1e-3
+    got_x = nv.nvfp4_quantize(x, global_scale=gs, stream=side)
+    got_y = nv.nvfp4_gemm(got_x, wq, "f32", stream=side)
+    got_o = nv.nvfp4_gemm_nvfp4_out(got_x, wq, gs, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    for r, g in zip(ref_x, got_x):
+        assert torch.equal(r, g)
+    assert torch.equal(ref_y, got_y)
+    for r, g in zip(ref_o, got_o):
+        assert torch.equal(r, g)
