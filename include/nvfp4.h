@@ -91,6 +91,24 @@ int nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t col
                    void* stream);
 
 /*
+ * nvfp4_quantize for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as nvfp4_quantize, without the
+ * workspace: the amax pass keeps its partial maxima (at most 4 KB) in a
+ * device array of the library's own, one per GPU, held until the process
+ * ends; the call allocates nothing.  Every call on one GPU shares that
+ * array, so calls that overlap on a GPU (concurrent streams, other host
+ * threads) race and must be ordered by the caller.  Shapes whose partial
+ * maxima would not fit return NVFP4_ERR_UNSUPPORTED (none do: the amax
+ * pass runs at most 1024 workgroups).  The first call on a device looks up
+ * the array's address there (no allocation); a failure of that lookup
+ * returns NVFP4_ERR_HIP.
+ */
+int nvfp4_quantize_noalloc(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                           int64_t ld_x, uint8_t* q, uint8_t* s, float* global_scale,
+                           unsigned flags, void* stream);
+
+/*
  * Dense NVFP4 GEMM (kernelindex, "NVFP4 linear layer"): for m < M, n < N
  *   y[m, n] = fl32(a_g * b_g) * sum_{k<K} A(m, k) * B(n, k)
  * with A(m, k) = E2M1(a_q nibble (m, k)) * E4M3(a_s[m, k/16]) and B the same

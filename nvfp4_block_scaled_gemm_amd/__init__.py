@@ -10,5 +10,5 @@ from ._lib import (  # noqa: F401
     Packed, load, nvfp4_gemm, nvfp4_gemm_nvfp4_out, nvfp4_gemm_nvfp4_out_raw, nvfp4_gemm_raw,
     nvfp4_grouped_gemm, nvfp4_grouped_gemm_gather_raw,
     nvfp4_grouped_gemm_raw,
-    nvfp4_quantize, nvfp4_quantize_raw, nvfp4_quantize_workspace_bytes,
+    nvfp4_quantize, nvfp4_quantize_noalloc_raw, nvfp4_quantize_raw, nvfp4_quantize_workspace_bytes,
 )

@@ -25,7 +25,7 @@ NVFP4_BF16 = 1
 NVFP4_GLOBAL_SCALE_GIVEN = 1
 
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
-            "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_nvfp4_out", "nvfp4_grouped_gemm",
+            "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_gemm", "nvfp4_gemm_nvfp4_out", "nvfp4_grouped_gemm",
             "nvfp4_grouped_gemm_gather")
 
 _lib = None
@@ -56,6 +56,9 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, p, ctypes.c_uint,
                                    p, sz, p]
     lib.nvfp4_quantize.restype = ctypes.c_int
+    lib.nvfp4_quantize_noalloc.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, p, ctypes.c_uint,
+                                           p]
+    lib.nvfp4_quantize_noalloc.restype = ctypes.c_int
     lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, ctypes.c_int, i64, p]
     lib.nvfp4_gemm.restype = ctypes.c_int
     lib.nvfp4_gemm_nvfp4_out.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p]
@@ -186,6 +189,12 @@ def nvfp4_quantize_raw(x, x_dtype, rows, cols, ld_x, q, s, global_scale, flags,
                        workspace, workspace_bytes, stream=None) -> int:
     return load().nvfp4_quantize(x, x_dtype, rows, cols, ld_x, q, s, global_scale, flags,
                                  workspace, workspace_bytes, _stream(stream))
+
+
+def nvfp4_quantize_noalloc_raw(x, x_dtype, rows, cols, ld_x, q, s, global_scale, flags,
+                               stream=None) -> int:
+    return load().nvfp4_quantize_noalloc(x, x_dtype, rows, cols, ld_x, q, s, global_scale, flags,
+                                         _stream(stream))
 
 
 def nvfp4_gemm_raw(M, N, K, a_q, a_s, a_g, b_q, b_s, b_g, y, y_dtype, ld_y,

@@ -124,6 +124,33 @@ int nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t col
                                          given, workspace, (hipStream_t)stream));
 }
 
+int nvfp4_quantize_noalloc(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                           int64_t ld_x, uint8_t* q, uint8_t* s, float* global_scale,
+                           unsigned flags, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (flags & ~NVFP4_GLOBAL_SCALE_GIVEN) return NVFP4_ERR_INVALID_ARG;
+  if (global_scale == nullptr) return NVFP4_ERR_INVALID_ARG;
+  if (rows > kMaxDim || cols > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (x == nullptr || q == nullptr || s == nullptr) return NVFP4_ERR_INVALID_ARG;
+  if (ld_x < cols) return NVFP4_ERR_INVALID_ARG;
+  const int64_t esz = x_dtype == NVFP4_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ld_x * esz) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(q, 8)) return NVFP4_ERR_UNSUPPORTED;
+  const bool given = (flags & NVFP4_GLOBAL_SCALE_GIVEN) != 0;
+  void* ws = nullptr;
+  if (!given) {
+    // the partial maxima must fit the library's array
+    if (nvfp4::quantize_workspace_bytes(rows, cols) > nvfp4::quantize_scratch_bytes())
+      return NVFP4_ERR_UNSUPPORTED;
+    const int e = from_hip(nvfp4::quantize_scratch(&ws));
+    if (e != NVFP4_OK) return e;
+  }
+  return from_hip(nvfp4::launch_quantize(x, (int)x_dtype, rows, cols, ld_x, q, s, global_scale,
+                                         given, ws, (hipStream_t)stream));
+}
+
 int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
                const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
                void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {

@@ -13,6 +13,11 @@ size_t quantize_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
                            uint8_t* q, uint8_t* s, float* gscale, bool scale_given,
                            void* workspace, hipStream_t stream);
+// The library's own quantise workspace (a device array, one per GPU): its
+// size in bytes, and its address on the current device (found once per
+// device with hipGetSymbolAddress).
+size_t quantize_scratch_bytes();
+hipError_t quantize_scratch(void** ptr);
 
 // Operand description of one packed NVFP4 matrix [rows, K].
 struct PackedOperand {

@@ -32,6 +32,8 @@
 #include "nvfp4_encode.h"
 #include "nvfp4_internal.h"
 
+#include <mutex>
+
 namespace nvfp4 {
 namespace {
 
@@ -166,13 +168,44 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   else encode_all<DT, 2>(x, rows, nblk_row, ld_x, q, s, P);
 }
 
+constexpr int kMaxPartials = 1024;  // the amax pass never runs more workgroups
+
 int amax_grid(int64_t nblocks) {
   int64_t g = (nblocks + kThreads - 1) / kThreads;
-  if (g > 1024) g = 1024;
+  if (g > kMaxPartials) g = kMaxPartials;
   return g < 1 ? 1 : (int)g;
 }
 
 }  // namespace
+
+// Workspace of nvfp4_quantize_noalloc: the amax pass's partial maxima, one
+// copy per GPU the library runs on, held until the process ends.  Every
+// call on a GPU shares it, so calls that overlap on one GPU race.  Nothing
+// in it needs clearing: each call writes every partial its encode pass
+// reads.  Host code must not pass the array's name to a kernel (on the host
+// it is only a stand-in); quantize_scratch() hands out its device address.
+static __device__ __align__(256) uint32_t scratch[kMaxPartials];
+
+size_t quantize_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t quantize_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with that device current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0) return 0;

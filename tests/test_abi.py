@@ -260,3 +260,28 @@ def test_output_buffer_checks_on_host():
             L._out(bad, 4, 8, torch.bfloat16, -1)
     with pytest.raises(ValueError):                                # another device
         L._out(torch.empty((4, 8), dtype=torch.bfloat16), 4, 8, torch.bfloat16, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cols=24), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(rows=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x_dtype=5), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(flags=2), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(global_scale=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(ld_x=16), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=P8), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(q=P4), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(rows=1 << 31), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(rows=0), nv.NVFP4_OK),
+])
+def test_quantize_noalloc_validation(kw, status):
+    """The no-allocation quantiser validates like nvfp4_quantize (no
+    workspace arguments) and touches nothing on an invalid call."""
+    args = dict(x=P16, x_dtype=nv.NVFP4_BF16, rows=4, cols=32, ld_x=32, q=P16, s=P16,
+                global_scale=P16, flags=0)
+    args.update(kw)
+    st = nv.load().nvfp4_quantize_noalloc(args["x"], args["x_dtype"], args["rows"], args["cols"],
+                                          args["ld_x"], args["q"], args["s"],
+                                          args["global_scale"], args["flags"], None)
+    assert st == status
