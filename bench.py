@@ -18,7 +18,8 @@ fp16 dense matrix-core peak, since that is the MFMA family the kernel
 issues.  ``decode`` holds the skinny M = 1, 16, 32 GEMMs over 16 rotating copies of W
 (604 MB, so the 256 MB Infinity Cache cannot hold them), timed as 128
 back-to-back launches between one pair of events, and ``moe_grouped``
-the two grouped expert GEMMs, each against HBM peak; ``mid_m`` GEMMs with
+the two grouped expert GEMMs, each against HBM peak, then both in one
+launch against the two calls back to back; ``mid_m`` GEMMs with
 M = 64 .. 1024 on the same rotating weights; ``large`` the
 M = N = K = 16384 outlier workload (quantiser on x alone, then the GEMM);
 ``library_reference`` torch's bf16 GEMM at the linear shape and a 1 GiB
@@ -321,6 +322,7 @@ def main():
     moe = {"tokens": wl.MOE_TOKENS, "experts": wl.MOE_EXPERTS, "topk": wl.MOE_TOPK,
            "rows_per_expert_min": int(routing.counts.min()),
            "rows_per_expert_max": int(routing.counts.max())}
+    layer = {}
     for proj, (n_, k_) in (("gate_up", wl.MOE_GATE_UP), ("down", wl.MOE_DOWN)):
         E = wl.MOE_EXPERTS
         bq = torch.empty((E, n_, k_ // 2), dtype=torch.uint8, device=dev)
@@ -363,7 +365,32 @@ def main():
             moe[name] = {"N": n_, "K": k_, "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
                          "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "tflops": round(2.0 * tot_ * n_ * k_ / (ms * 1e-3) / 1e12, 2)}
-        del bq, bs, bg, a, ym, experts, a_op
+        # kept for the layer timing below: the gate_up call through the
+        # routing index and the down call on grouped rows
+        layer[proj] = dict(m_offsets=off, total_m=total, b=experts, out_dtype="bf16", y=ym,
+                           a=nv.Packed(tuple(xq)) if proj == "gate_up" else nv.Packed(tuple(a)),
+                           row_index=rt.to(torch.int32) if proj == "gate_up" else None)
+        del bq, bs, bg, a, a_op
+
+    # Both projections of the layer: one launch over the union of their
+    # work items against the two calls back to back.
+    calls = [layer["gate_up"], layer["down"]]
+    timed(lambda i: nv.nvfp4_grouped_gemm_multi(calls), 20)
+    one_ms = timed(lambda i: nv.nvfp4_grouped_gemm_multi(calls), 20)
+
+    def two(i):
+        for c in calls:
+            nv.nvfp4_grouped_gemm(**c)
+    timed(two, 20)
+    two_ms = timed(two, 20)
+    nbytes = moe["gate_up_gather"]["algorithmic_bytes"] + moe["down"]["algorithmic_bytes"]
+    gbs = nbytes / (one_ms * 1e-3) / 1e9
+    moe["layer_one_launch"] = {"us": round(one_ms * 1e3, 2), "algorithmic_bytes": nbytes,
+                               "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                               "two_calls_us": round(two_ms * 1e3, 2),
+                               "sum_of_single_calls_us": round(moe["gate_up_gather"]["us"]
+                                                               + moe["down"]["us"], 2)}
+    del calls, layer
 
     # Large outlier workload M = N = K = 16384 (1 % of entries x50): the
     # quantiser on x timed alone (two reads of x + the packed writes), then

@@ -189,6 +189,51 @@ int nvfp4_grouped_gemm_gather(int32_t G, const int32_t* m_offsets, const int32_t
                               const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
                               void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream);
 
+/*
+ * Several independent grouped GEMMs in one launch.  A mixture-of-experts
+ * layer runs its gate_up and down projections as grouped GEMMs over the
+ * same routing ("The Moment of Synthesis", "The Reasoning Process":
+ * grouping is the lever for tiny per-expert batches; "The Moment of
+ * Recalibration", "The Broader Narrative Arc": persistent grouped kernels);
+ * one persistent launch over the union of their (expert, weight tile) work
+ * shares the launch ramp, the per-CU fill and the tail.  The projections
+ * are independent here (each has its own activation; the operation between
+ * them is outside this library).
+ *
+ * Each element of `problems` (a HOST array of `count` entries, 0 <= count
+ * <= NVFP4_GROUPED_MAX_PROBLEMS) describes one call with exactly the
+ * meaning of nvfp4_grouped_gemm (row_index == NULL) or
+ * nvfp4_grouped_gemm_gather (row_index != NULL, a_rows = rows of a); with
+ * row_index == NULL, a_rows must be 0 or total_m.  Results are those of
+ * the separate calls, bit for bit.  Outputs of different problems must not
+ * overlap.  Every problem is validated before anything is enqueued; any
+ * error leaves all outputs untouched.  Problems the streaming kernel cannot
+ * take (K % 512 != 0, unaligned rows, operands of 4 GiB or more) make the
+ * call run each problem on its own.
+ */
+#define NVFP4_GROUPED_MAX_PROBLEMS 4
+
+typedef struct {
+  int32_t G;                  /* groups (experts)                                */
+  const int32_t* m_offsets;   /* DEVICE int32 [G+1]                              */
+  const int32_t* row_index;   /* DEVICE int32 [total_m], or NULL                 */
+  int64_t total_m;            /* m_offsets[G]                                    */
+  int64_t a_rows;             /* rows of a when row_index != NULL                */
+  int64_t N, K;
+  const uint8_t* a_q;         /* [a_rows, K/2]  (total_m rows without row_index) */
+  const uint8_t* a_s;         /* [a_rows, K/16]                                  */
+  const float* a_g;           /* DEVICE fp32 scalar                              */
+  const uint8_t* b_q;         /* [G, N, K/2]                                     */
+  const uint8_t* b_s;         /* [G, N, K/16]                                    */
+  const float* b_g;           /* DEVICE fp32 [G]                                 */
+  void* y;                    /* [total_m, N], row stride ld_y                   */
+  nvfp4_dtype y_dtype;
+  int64_t ld_y;
+} nvfp4_grouped_problem;
+
+int nvfp4_grouped_gemm_multi(int32_t count, const nvfp4_grouped_problem* problems,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

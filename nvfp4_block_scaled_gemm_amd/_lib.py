@@ -26,9 +26,20 @@ NVFP4_GLOBAL_SCALE_GIVEN = 1
 
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
             "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_gemm", "nvfp4_gemm_nvfp4_out", "nvfp4_grouped_gemm",
-            "nvfp4_grouped_gemm_gather")
+            "nvfp4_grouped_gemm_gather", "nvfp4_grouped_gemm_multi")
+NVFP4_GROUPED_MAX_PROBLEMS = 4
 
 _lib = None
+
+
+class GroupedProblem(ctypes.Structure):
+    """nvfp4_grouped_problem of include/nvfp4.h (one grouped GEMM)."""
+    _fields_ = [("G", ctypes.c_int32), ("m_offsets", ctypes.c_void_p),
+                ("row_index", ctypes.c_void_p), ("total_m", ctypes.c_int64),
+                ("a_rows", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a_q", ctypes.c_void_p), ("a_s", ctypes.c_void_p), ("a_g", ctypes.c_void_p),
+                ("b_q", ctypes.c_void_p), ("b_s", ctypes.c_void_p), ("b_g", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("y_dtype", ctypes.c_int), ("ld_y", ctypes.c_int64)]
 
 
 class Nvfp4Error(RuntimeError):
@@ -69,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_grouped_gemm_gather.argtypes = [i32, p, p, i64, i64, i64, i64, p, p, p, p, p, p,
                                               p, ctypes.c_int, i64, p]
     lib.nvfp4_grouped_gemm_gather.restype = ctypes.c_int
+    lib.nvfp4_grouped_gemm_multi.argtypes = [i32, ctypes.POINTER(GroupedProblem), p]
+    lib.nvfp4_grouped_gemm_multi.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -326,13 +339,8 @@ def nvfp4_gemm_nvfp4_out(a, b, y_g: torch.Tensor, out=None, stream=None):
     return q, s, y_g
 
 
-def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: str = "bf16",
-                       y: torch.Tensor | None = None, stream=None,
-                       row_index: torch.Tensor | None = None):
-    """m_offsets int32 [G+1] (GPU); a = (q [total_m, K/2], s, g [1]);
-    b = (q [G, N, K/2], s [G, N, K/16], g [G]) -> y [total_m, N].
-    With row_index (int32 [total_m], GPU), grouped row r reads row
-    row_index[r] of a = (q [a_rows, K/2], s, g) instead (no gathered copy)."""
+def _grouped_problem(m_offsets, total_m, a, b, out_dtype, y, stream, row_index):
+    """Checks one grouped call's tensors; returns (GroupedProblem, y, dev)."""
     a, b = _packed(a), _packed(b)
     _need(len(b.lead) == 1 and not a.lead and a.K == b.K and a.dev == b.dev,
           "b: [G, N, K/2] packed experts and a: packed rows with the same K, on one GPU")
@@ -349,19 +357,64 @@ def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: s
         with _on_stream(stream, b.dev):
             y = torch.empty((total_m, N), dtype=tdt, device=b_q.device)
     ld_y = _out(y, total_m, N, tdt, b.dev)
-    stream = _stream(stream, b.dev)
+    a_rows = 0
+    if row_index is not None:
+        _need(row_index.dtype == torch.int32 and row_index.numel() == total_m
+              and row_index.is_contiguous(), "row_index: total_m contiguous int32")
+        _on_dev(row_index, b.dev, "row_index")
+        a_rows = a_q.shape[0]
+    prob = GroupedProblem(G, _ptr(m_offsets), _ptr(row_index) if row_index is not None else None,
+                          total_m, a_rows, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q),
+                          _ptr(b_s), _ptr(b_g), _ptr(y), code, ld_y)
+    return prob, y, b.dev
+
+
+def nvfp4_grouped_gemm(m_offsets: torch.Tensor, total_m: int, a, b, out_dtype: str = "bf16",
+                       y: torch.Tensor | None = None, stream=None,
+                       row_index: torch.Tensor | None = None):
+    """m_offsets int32 [G+1] (GPU); a = (q [total_m, K/2], s, g [1]);
+    b = (q [G, N, K/2], s [G, N, K/16], g [G]) -> y [total_m, N].
+    With row_index (int32 [total_m], GPU), grouped row r reads row
+    row_index[r] of a = (q [a_rows, K/2], s, g) instead (no gathered copy)."""
+    p, y, dev = _grouped_problem(m_offsets, total_m, a, b, out_dtype, y, stream, row_index)
+    stream = _stream(stream, dev)
     if row_index is None:
-        st = nvfp4_grouped_gemm_raw(G, _ptr(m_offsets), total_m, N, K, _ptr(a_q), _ptr(a_s),
-                                    _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
-                                    ld_y, stream)
+        st = nvfp4_grouped_gemm_raw(p.G, p.m_offsets, total_m, p.N, p.K, p.a_q, p.a_s, p.a_g,
+                                    p.b_q, p.b_s, p.b_g, p.y, p.y_dtype, p.ld_y, stream)
         _check("nvfp4_grouped_gemm", st)
         return y
-    _need(row_index.dtype == torch.int32 and row_index.numel() == total_m
-          and row_index.is_contiguous(), "row_index: total_m contiguous int32")
-    _on_dev(row_index, b.dev, "row_index")
-    st = nvfp4_grouped_gemm_gather_raw(G, _ptr(m_offsets), _ptr(row_index), total_m,
-                                       a_q.shape[0], N, K, _ptr(a_q), _ptr(a_s), _ptr(a_g),
-                                       _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(y), code,
-                                       ld_y, stream)
+    st = nvfp4_grouped_gemm_gather_raw(p.G, p.m_offsets, p.row_index, total_m, p.a_rows, p.N,
+                                       p.K, p.a_q, p.a_s, p.a_g, p.b_q, p.b_s, p.b_g, p.y,
+                                       p.y_dtype, p.ld_y, stream)
     _check("nvfp4_grouped_gemm_gather", st)
     return y
+
+
+def nvfp4_grouped_gemm_multi_raw(problems, stream=None) -> int:
+    """problems: a sequence of GroupedProblem (host structures)."""
+    arr = (GroupedProblem * max(len(problems), 1))(*problems)
+    return load().nvfp4_grouped_gemm_multi(len(problems), arr, _stream(stream))
+
+
+def nvfp4_grouped_gemm_multi(calls, stream=None):
+    """Several grouped GEMMs in one launch.  `calls` is a sequence (at most
+    NVFP4_GROUPED_MAX_PROBLEMS) of dicts holding nvfp4_grouped_gemm's
+    arguments (m_offsets, total_m, a, b and optionally out_dtype, y,
+    row_index); returns their outputs, equal bit for bit to those of the
+    separate calls."""
+    _need(len(calls) <= NVFP4_GROUPED_MAX_PROBLEMS,
+          f"at most {NVFP4_GROUPED_MAX_PROBLEMS} grouped problems per launch")
+    probs, ys, devs = [], [], set()
+    for c in calls:
+        p, y, dev = _grouped_problem(c["m_offsets"], c["total_m"], c["a"], c["b"],
+                                     c.get("out_dtype", "bf16"), c.get("y"), stream,
+                                     c.get("row_index"))
+        probs.append(p)
+        ys.append(y)
+        devs.add(dev)
+    if not probs:
+        return ys
+    _need(len(devs) == 1, "all problems on one GPU")
+    st = nvfp4_grouped_gemm_multi_raw(probs, _stream(stream, devs.pop()))
+    _check("nvfp4_grouped_gemm_multi", st)
+    return ys

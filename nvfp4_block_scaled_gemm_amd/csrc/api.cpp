@@ -34,29 +34,52 @@ nvfp4::OperandAlign align_of(const uint8_t* q, const uint8_t* s) {
   return {aligned(q, 16), aligned(s, 8), aligned(s, 16)};
 }
 
-// Shared body of the two grouped entry points (row_index == nullptr: rows
-// of A are the grouped rows themselves, a_rows == total_m).
-int grouped_impl(int32_t G, const int32_t* m_offsets, const int32_t* row_index, int64_t total_m,
-                 int64_t a_rows, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
-                 const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
-                 void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {
+// Checks of one grouped problem (row_index == nullptr: rows of A are the
+// grouped rows themselves, a_rows == total_m).  Returns NVFP4_OK, an error,
+// or 1 for "valid, nothing to do".
+int grouped_check(int32_t G, const int32_t* m_offsets, int64_t total_m, int64_t a_rows,
+                  int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                  const uint8_t* b_q, const uint8_t* b_s, const float* b_g, const void* y,
+                  nvfp4_dtype y_dtype, int64_t ld_y) {
   if (G < 0 || total_m < 0 || N < 0 || K < 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
   if (G == 0 && total_m != 0) return NVFP4_ERR_INVALID_ARG;
   if (total_m > kMaxDim || a_rows > kMaxDim || N > kMaxDim || K > kMaxDim)
     return NVFP4_ERR_UNSUPPORTED;
-  if (total_m == 0 || N == 0) return NVFP4_OK;
+  if (total_m == 0 || N == 0) return 1;
   if (m_offsets == nullptr || y == nullptr || ld_y < N) return NVFP4_ERR_INVALID_ARG;
   if (!operand_ok(a_rows, K, a_q, a_s, a_g) || !operand_ok(N, K, b_q, b_s, b_g))
     return NVFP4_ERR_INVALID_ARG;
-  const nvfp4::PackedOperand a{a_q, a_s, a_g}, b{b_q, b_s, b_g};
-  hipStream_t st = (hipStream_t)stream;
-  if (K > 0 && tiled_ok(K, a_q, a_s, 512) && tiled_ok(K, b_q, b_s, 512) &&
-      offsets32_ok(total_m, K) && offsets32_ok(a_rows, K) && offsets32_ok(N, K))
-    return from_hip(nvfp4::launch_gemm_grouped(G, m_offsets, row_index, total_m, a_rows, N, K, a,
-                                               b, y, (int)y_dtype, ld_y, st));
-  return from_hip(nvfp4::launch_gemm_grouped_generic(G, m_offsets, row_index, total_m, a_rows, N,
-                                                     K, a, b, y, (int)y_dtype, ld_y, st));
+  return NVFP4_OK;
+}
+
+// The streaming grouped kernel takes K % 512 == 0, aligned rows and
+// operands whose byte offsets fit 32 bits; anything else runs the general
+// kernel.
+bool grouped_streams(const nvfp4::GroupedProblem& g) {
+  return g.K > 0 && tiled_ok(g.K, g.a.q, g.a.s, 512) && tiled_ok(g.K, g.b.q, g.b.s, 512) &&
+         offsets32_ok(g.total_m, g.K) && offsets32_ok(g.a_rows, g.K) && offsets32_ok(g.N, g.K);
+}
+
+int grouped_run(const nvfp4::GroupedProblem& g, hipStream_t st) {
+  if (grouped_streams(g)) return from_hip(nvfp4::launch_gemm_grouped_multi(1, &g, st));
+  return from_hip(nvfp4::launch_gemm_grouped_generic(g.G, g.m_offsets, g.row_index, g.total_m,
+                                                     g.a_rows, g.N, g.K, g.a, g.b, g.y, g.y_dtype,
+                                                     g.ld_y, st));
+}
+
+// Shared body of the two grouped entry points.
+int grouped_impl(int32_t G, const int32_t* m_offsets, const int32_t* row_index, int64_t total_m,
+                 int64_t a_rows, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+                 const float* a_g, const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                 void* y, nvfp4_dtype y_dtype, int64_t ld_y, void* stream) {
+  const int v = grouped_check(G, m_offsets, total_m, a_rows, N, K, a_q, a_s, a_g, b_q, b_s, b_g,
+                              y, y_dtype, ld_y);
+  if (v != NVFP4_OK) return v == 1 ? NVFP4_OK : v;
+  const nvfp4::GroupedProblem g{G, m_offsets, row_index, total_m, a_rows, N, K,
+                                nvfp4::PackedOperand{a_q, a_s, a_g},
+                                nvfp4::PackedOperand{b_q, b_s, b_g}, y, (int)y_dtype, ld_y};
+  return grouped_run(g, (hipStream_t)stream);
 }
 
 // Shape dispatch of the dense GEMM (both entry points, so an NVFP4 output
@@ -198,6 +221,42 @@ int nvfp4_grouped_gemm_gather(int32_t G, const int32_t* m_offsets, const int32_t
   if (total_m > 0 && row_index == nullptr) return NVFP4_ERR_INVALID_ARG;
   return grouped_impl(G, m_offsets, row_index, total_m, a_rows, N, K, a_q, a_s, a_g, b_q, b_s, b_g,
                       y, y_dtype, ld_y, stream);
+}
+
+int nvfp4_grouped_gemm_multi(int32_t count, const nvfp4_grouped_problem* problems,
+                             void* stream) {
+  if (count < 0 || count > NVFP4_GROUPED_MAX_PROBLEMS) return NVFP4_ERR_INVALID_ARG;
+  if (count == 0) return NVFP4_OK;
+  if (problems == nullptr) return NVFP4_ERR_INVALID_ARG;
+  nvfp4::GroupedProblem gs[NVFP4_GROUPED_MAX_PROBLEMS];
+  int n = 0;
+  bool all_stream = true;
+  // every problem is checked before anything is enqueued
+  for (int i = 0; i < count; ++i) {
+    const nvfp4_grouped_problem& p = problems[i];
+    const int64_t a_rows = p.row_index != nullptr ? p.a_rows : p.total_m;
+    if (p.row_index != nullptr && p.a_rows < 0) return NVFP4_ERR_INVALID_ARG;
+    if (p.row_index == nullptr && p.a_rows != 0 && p.a_rows != p.total_m)
+      return NVFP4_ERR_INVALID_ARG;
+    const int v = grouped_check(p.G, p.m_offsets, p.total_m, a_rows, p.N, p.K, p.a_q, p.a_s,
+                                p.a_g, p.b_q, p.b_s, p.b_g, p.y, p.y_dtype, p.ld_y);
+    if (v == 1) continue;  // valid, empty
+    if (v != NVFP4_OK) return v;
+    gs[n] = nvfp4::GroupedProblem{p.G, p.m_offsets, p.row_index, p.total_m, a_rows, p.N, p.K,
+                                  nvfp4::PackedOperand{p.a_q, p.a_s, p.a_g},
+                                  nvfp4::PackedOperand{p.b_q, p.b_s, p.b_g}, p.y,
+                                  (int)p.y_dtype, p.ld_y};
+    all_stream = all_stream && grouped_streams(gs[n]);
+    ++n;
+  }
+  if (n == 0) return NVFP4_OK;
+  const hipStream_t st = (hipStream_t)stream;
+  if (all_stream) return from_hip(nvfp4::launch_gemm_grouped_multi(n, gs, st));
+  for (int i = 0; i < n; ++i) {
+    const int e = grouped_run(gs[i], st);
+    if (e != NVFP4_OK) return e;
+  }
+  return NVFP4_OK;
 }
 
 }  // extern "C"

@@ -38,6 +38,14 @@
 //    the four weight fragments.
 //  * After the last slice of an item-chunk the wave scales by ga * gb[e] and
 //    stores its 64 x ntok outputs, four consecutive columns per store.
+//  * One launch can carry several independent grouped GEMMs (up to
+//    kMaxProblems, e.g. a mixture-of-experts layer's gate_up and down
+//    projections): their items are numbered one after the other and the
+//    waves walk the union, so the launch ramp, the per-CU fill and the tail
+//    are shared.  A wave takes its items problem by problem, each through a
+//    copy of the pipeline specialised for that problem (drained in between),
+//    so the problem's sizes and operand descriptors sit in scalar registers
+//    as in a single-problem launch.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -71,6 +79,7 @@ constexpr int kScLoads = kRows / 32;             // 16-byte DMAs of scales (32 r
 constexpr int kLoadsPerJob = kNibLoads + kScLoads + 10;  // memory instructions per job
 static_assert(kFrags % 2 == 0, "scale DMAs cover 32 rows");
 constexpr uint32_t kOob = 0xFFFFFFF0u;           // offset past every operand (reads zero)
+constexpr int kMaxProblems = kGroupedMaxProblems;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -92,9 +101,57 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// A wave's position in its job sequence (all fields wave-uniform).
+// One grouped GEMM of a launch (every field uniform).
+struct Problem {
+  const int32_t* m_offsets;  // [G + 1]
+  const int32_t* row_index;  // nullptr: grouped row r reads activation row r
+  const uint8_t* a_q;
+  const uint8_t* a_s;
+  const float* a_g;
+  const uint8_t* b_q;
+  const uint8_t* b_s;
+  const float* b_g;
+  void* y;
+  int64_t ld_y;
+  int64_t total_m;
+  int64_t a_rows;            // rows of the activation operand
+  int N, K, nunits, tiles;
+  int item_base, n_items;    // the problem's items: [item_base, item_base + n_items)
+  int y_dtype;
+  uint32_t y_bytes;          // extent of y when below 4 GiB and its rows take
+                             // 8-byte (bf16) / 16-byte (fp32) stores, else 0
+};
+
+struct Problems {
+  Problem p[kMaxProblems];
+  int count, n_items, stride;  // problems, items of all of them, grid stride
+};
+
+// The launch's problem list is its only argument, so it starts the
+// kernel-argument segment; problem pi's fields are read from there with
+// scalar loads (indexing the by-value argument instead would copy it to
+// private memory).  pi is fixed across a problem's loop, so the loads are
+// loop-invariant.
+typedef const Problems __attribute__((address_space(4)))* ProblemsPtr;
+typedef const Problem __attribute__((address_space(4)))& ProblemRef;
+__device__ __forceinline__ ProblemRef problem(int pi) {
+  return ((ProblemsPtr)__builtin_amdgcn_kernarg_segment_ptr())->p[pi];
+}
+
+// Read-only inputs read at uniform addresses (routing offsets and indices,
+// global scales) are addressed through the constant address space, so
+// they come in through the scalar cache and their wait never drains the
+// vector loads in flight.  (Reached through the problem struct, the
+// compiler cannot otherwise tell that the output stores leave them alone.)
+template <typename T>
+__device__ __forceinline__ const T __attribute__((address_space(4)))* scalar_ptr(const T* p) {
+  return (const T __attribute__((address_space(4)))*)p;
+}
+
+// A wave's position in its job sequence over one problem (all fields
+// wave-uniform).
 struct Cursor {
-  int item;              // global item id (>= n_items: finished)
+  int item;              // item of the problem (>= n_items: finished)
   int e, n0;             // expert and first weight row of the item
   int r0, r1;            // the expert's token rows [r0, r1)
   int c0;                // first token row of the current chunk
@@ -104,52 +161,49 @@ struct Cursor {
                          // fragment (kOob: no row)
 };
 
-struct Shape {
-  int N, nunits, tiles, n_items, stride;
-  int64_t total_m;
-  int64_t a_rows;        // rows of the activation operand
-  uint32_t y_bytes;      // extent of y when below 4 GiB and its rows take
-                         // 8-byte (bf16) / 16-byte (fp32) stores, else 0
-};
-
 // Expert rows of item `it`, clamped into [0, total_m) whatever the offsets
 // hold.  The expert index is made explicitly scalar so the two offsets come
 // in through the scalar cache (their wait never drains the vector loads).
-__device__ __forceinline__ void item_rows(const Shape& sh, const int32_t* __restrict__ m_offsets,
-                                          int it, Cursor& c) {
+__device__ __forceinline__ void item_rows(ProblemRef P, int it, Cursor& c) {
   c.item = it;
-  c.e = __builtin_amdgcn_readfirstlane(it / sh.tiles);
-  c.n0 = (it - c.e * sh.tiles) * kRows;
+  c.e = __builtin_amdgcn_readfirstlane(it / P.tiles);
+  c.n0 = (it - c.e * P.tiles) * kRows;
+  const auto m_offsets = scalar_ptr(P.m_offsets);
   int64_t a = m_offsets[c.e], b = m_offsets[c.e + 1];
-  a = a < 0 ? 0 : (a > sh.total_m ? sh.total_m : a);
-  b = b < a ? a : (b > sh.total_m ? sh.total_m : b);
+  a = a < 0 ? 0 : (a > P.total_m ? P.total_m : a);
+  b = b < a ? a : (b > P.total_m ? P.total_m : b);
   c.r0 = (int)a;
   c.r1 = (int)b;
 }
 
 // First item at or after `it` (stepping by the grid stride) with tokens.
-__device__ __forceinline__ void seek_item(const Shape& sh, const int32_t* __restrict__ m_offsets,
-                                          int it, Cursor& c) {
-  for (; it < sh.n_items; it += sh.stride) {
-    item_rows(sh, m_offsets, it, c);
+// Both exits store the same fields, so the cursor stays in registers.
+__device__ __forceinline__ void seek_item(ProblemRef P, int it, int stride, Cursor& c) {
+  const int n_items = P.n_items;
+  bool found = false;
+  for (; it < n_items; it += stride) {
+    item_rows(P, it, c);
     if (c.r1 > c.r0) {
-      c.c0 = c.r0;
-      c.u = 0;
-      c.rows_c0 = -1;
-      return;
+      found = true;
+      break;
     }
   }
-  c.item = sh.n_items;
+  if (!found) {
+    c.item = n_items;
+    c.e = c.n0 = c.r0 = c.r1 = 0;
+  }
+  c.c0 = c.r0;
+  c.u = 0;
+  c.rows_c0 = -1;
 }
 
-__device__ __forceinline__ void advance(const Shape& sh, const int32_t* __restrict__ m_offsets,
-                                        Cursor& c) {
-  if (c.item >= sh.n_items) return;
-  if (++c.u < sh.nunits) return;
+__device__ __forceinline__ void advance(ProblemRef P, int stride, Cursor& c) {
+  if (c.item >= P.n_items) return;
+  if (++c.u < P.nunits) return;
   c.u = 0;
   c.c0 += 32;
   if (c.c0 < c.r1) return;
-  seek_item(sh, m_offsets, c.item + sh.stride, c);
+  seek_item(P, c.item + stride, stride, c);
 }
 
 __device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
@@ -159,25 +213,23 @@ struct XFrags {
   u32x2 s[2];     // their 8 scale bytes
 };
 
-// GATHER: grouped row r reads activation row row_index[r] (an index outside
-// [0, a_rows) reads as a zero row); otherwise row r itself.
+// The items of problem pi that fall to wave `w` of the grid (global item
+// ids w, w + stride, ...), through its own load/compute pipeline.  GATHER
+// (the problem has a routing index): grouped row r reads activation row
+// row_index[r] (an index outside [0, a_rows) reads as a zero row);
+// otherwise grouped row r is activation row r.
 template <bool GATHER>
-__global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
-    Shape sh, const int32_t* __restrict__ m_offsets, const int32_t* __restrict__ row_index, int K,
-    const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
-    const float* __restrict__ a_g, const uint8_t* __restrict__ b_q,
-    const uint8_t* __restrict__ b_s, const float* __restrict__ b_g, void* __restrict__ y,
-    int y_dtype, int64_t ld_y) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+__device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* ring) {
+  ProblemRef P = problem(pi);
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lq = lane >> 4;
-  uint8_t* ring = smem + wave * kWaveLds;
-
+  const int K = P.K;
   const uint32_t qrow = (uint32_t)(K / 2), srow = (uint32_t)(K / 16);
-  const uint32_t wq_bytes = (uint32_t)sh.N * qrow, ws_bytes = (uint32_t)sh.N * srow;
-  const uint32_t xq_bytes = (uint32_t)sh.a_rows * qrow, xs_bytes = (uint32_t)sh.a_rows * srow;
-  const float ga = a_g[0];
+  const uint32_t wq_bytes = (uint32_t)P.N * qrow, ws_bytes = (uint32_t)P.N * srow;
+  const uint32_t xq_bytes = (uint32_t)P.a_rows * qrow, xs_bytes = (uint32_t)P.a_rows * srow;
+  const uint8_t* __restrict__ a_q = P.a_q;
+  const uint8_t* __restrict__ a_s = P.a_s;
+  const auto row_index = scalar_ptr(P.row_index);  // used with GATHER
 
   // Load offsets = a per-lane constant + a scalar per job.  Weight nibble
   // load k (16 B per lane) covers item rows 4k .. 4k+3: lane L takes row
@@ -197,13 +249,14 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
 
   // Activation rows of the chunk at c.c0 for this lane's two token
   // fragments (chunk rows 16g + li), as byte offsets of the row starts.
-  // With GATHER the chunk's 32 indices come through the scalar cache (so
-  // their wait never drains the vector loads) and each lane picks its own.
+  // With a routing index the chunk's 32 indices come through the scalar
+  // cache (so their wait never drains the vector loads) and each lane picks
+  // its own.
   auto chunk_rows = [&](Cursor& c) {
     int src[2] = {c.c0 + li, c.c0 + 16 + li};
     if constexpr (GATHER) {
       const int base = __builtin_amdgcn_readfirstlane(c.c0);
-      const int last = (int)sh.total_m - 1;
+      const int last = (int)P.total_m - 1;
       int v0 = 0, v1 = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -216,7 +269,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const bool ok = c.c0 + 16 * g + li < c.r1 && src[g] >= 0 && (int64_t)src[g] < sh.a_rows;
+      const bool ok = c.c0 + 16 * g + li < c.r1 && src[g] >= 0 && (int64_t)src[g] < P.a_rows;
       c.xq[g] = ok ? (uint32_t)src[g] * qrow : kOob;
       c.xs[g] = ok ? (uint32_t)src[g] * srow : kOob;
     }
@@ -230,11 +283,11 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
   // pads with loads of expert 0's first slice.
   auto issue = [&](Cursor& c, auto sc) {
     constexpr int S = decltype(sc)::value;
-    const bool live = c.item < sh.n_items;
+    const bool live = c.item < P.n_items;
     if (live && c.rows_c0 != c.c0) chunk_rows(c);  // uniform
     const int e = live ? c.e : 0;
-    const uint8_t* wq = b_q + (int64_t)e * sh.N * qrow;
-    const uint8_t* ws = b_s + (int64_t)e * sh.N * srow;
+    const uint8_t* wq = P.b_q + (int64_t)e * P.N * qrow;
+    const uint8_t* ws = P.b_s + (int64_t)e * P.N * srow;
     const uint32_t wq_job = live ? (uint32_t)c.n0 * qrow + (uint32_t)c.u * kRowNib : 0u;
     const uint32_t ws_job = live ? (uint32_t)c.n0 * srow + (uint32_t)c.u * kRowSc : 0u;
     const uint32_t xq_job = (uint32_t)c.u * kRowNib + (uint32_t)lq * 64u;
@@ -318,13 +371,16 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    if (c.u == sh.nunits - 1) {
+    if (c.u == P.nunits - 1) {
       // acc[f][g] reg r: weight row n0 + 16f + 4*lq + r, token c0 + 16g + li
-      const float alpha = ga * b_g[c.e];
-      if (sh.y_bytes != 0 && c.n0 + kRows <= sh.N) {  // uniform
+      const float alpha = scalar_ptr(P.a_g)[0] * scalar_ptr(P.b_g)[c.e];
+      void* __restrict__ y = P.y;
+      const int64_t ld_y = P.ld_y;
+      const int y_dtype = P.y_dtype;
+      if (P.y_bytes != 0 && c.n0 + kRows <= P.N) {  // uniform
         // the lane's four consecutive outputs of a token in one store;
         // tokens outside the chunk get an offset past the output (no write)
-        const auto ry = rsrc(y, sh.y_bytes);
+        const auto ry = rsrc(y, P.y_bytes);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const int tok = 16 * g + li;
@@ -353,7 +409,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int n = c.n0 + 16 * f + 4 * lq + r;
-              if (tok < ntok && n < sh.N)
+              if (tok < ntok && n < P.N)
                 store_out(y, (int64_t)(c.c0 + tok) * ld_y + n, acc[f][g][r] * alpha, y_dtype);
             }
             acc[f][g] = f32x4{0, 0, 0, 0};
@@ -362,39 +418,56 @@ __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(
     }
   };
 
-  Shape shl = sh;
+  // the problem's first item with global id = w modulo the grid stride
+  int first = (w - P.item_base) % stride;
+  first += first < 0 ? stride : 0;
   Cursor lc, cc;
   lc.rows_c0 = -1;
-  seek_item(shl, m_offsets, blockIdx.x * kWaves + wave, lc);
+  seek_item(P, first, stride, lc);
   cc = lc;
+  if (cc.item >= P.n_items) return;  // nothing of this problem for the wave
   static_for<kSlots - 1>([&](auto sc) {
     issue(lc, sc);
-    advance(shl, m_offsets, lc);
+    advance(P, stride, lc);
   });
   // jobs rotate through the slots; the loads of job j + kSlots - 1 go out
   // before job j waits for its own (the younger jobs may stay in flight)
-  bool more = cc.item < shl.n_items;
+  bool more = true;
   while (more) {
     static_for<kSlots>([&](auto sc) {
       constexpr int S = decltype(sc)::value;
       if (!more) return;
       issue(lc, std::integral_constant<int, (S + kSlots - 1) % kSlots>{});
-      advance(shl, m_offsets, lc);
+      advance(P, stride, lc);
       wait_vmcnt<(kSlots - 1) * kLoadsPerJob>();
       compute(cc, sc);
-      advance(shl, m_offsets, cc);
-      more = cc.item < shl.n_items;
+      advance(P, stride, cc);
+      more = cc.item < P.n_items;
     });
   }
-  wait_vmcnt<0>();  // padding loads land before the wave exits
+  wait_vmcnt<0>();  // padding loads land before the next problem reuses the ring
+}
+
+// The waves of the grid walk the union of the problems' items with a fixed
+// stride, problem by problem; each problem runs its own pipeline (drained
+// between problems), so its operand descriptors stay in scalar registers.
+__global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(const Problems ps) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* ring = smem + wave * kWaveLds;
+  const int w = blockIdx.x * kWaves + wave;
+  for (int pi = 0; pi < ps.count; ++pi) {
+    if (problem(pi).row_index != nullptr)  // uniform
+      run_problem<true>(pi, w, ps.stride, ring);
+    else
+      run_problem<false>(pi, w, ps.stride, ring);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
-                               int64_t total_m, int64_t a_rows, int64_t N, int64_t K,
-                               PackedOperand a, PackedOperand b, void* y, int y_dtype,
-                               int64_t ld_y, hipStream_t stream) {
+hipError_t launch_gemm_grouped_multi(int count, const GroupedProblem* probs, hipStream_t stream) {
+  if (count < 1 || count > kMaxProblems) return hipErrorInvalidValue;
   static int num_cu = 0;  // compute units of the current device (one query per process)
   if (num_cu == 0) {
     int dev = 0, n = 0;
@@ -403,30 +476,45 @@ hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_
       n = 256;
     num_cu = n;
   }
-  const int64_t tiles = (N + kRows - 1) / kRows;
-  const int64_t n_items = tiles * G;
-  if (n_items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  Problems ps{};
+  int64_t items = 0;
+  for (int i = 0; i < count; ++i) {
+    const GroupedProblem& g = probs[i];
+    Problem& P = ps.p[i];
+    const int64_t tiles = (g.N + kRows - 1) / kRows;
+    const int64_t n_items = tiles * g.G;
+    // whole 4-column groups of a row go out in one store when the rows are
+    // aligned for it and the output's byte extent fits 32-bit offsets
+    const int es = g.y_dtype == 0 ? 4 : 2;
+    const int64_t extent = g.total_m > 0 ? ((g.total_m - 1) * g.ld_y + g.N) * es : 0;
+    const bool aligned = (reinterpret_cast<uintptr_t>(g.y) % (4 * es)) == 0 && g.ld_y % 4 == 0;
+    P = Problem{g.m_offsets, g.row_index, g.a.q, g.a.s, g.a.g, g.b.q, g.b.s, g.b.g, g.y, g.ld_y,
+                g.total_m, g.row_index != nullptr ? g.a_rows : g.total_m, (int)g.N, (int)g.K,
+                (int)(g.K / kJobK), (int)tiles, (int)items, (int)n_items, g.y_dtype,
+                aligned && extent < (int64_t)0xFFFFFFF0 ? (uint32_t)extent : 0u};
+    items += n_items;
+    if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  }
+  if (items == 0) return hipSuccess;
   const int smem = kWaves * kWaveLds;
-  auto kern = row_index != nullptr ? gemm_grouped_kernel<true> : gemm_grouped_kernel<false>;
-  static const hipError_t attr0 = hipFuncSetAttribute(
-      (const void*)gemm_grouped_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-  static const hipError_t attr1 = hipFuncSetAttribute(
-      (const void*)gemm_grouped_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-  if (attr0 != hipSuccess) return attr0;
-  if (attr1 != hipSuccess) return attr1;
-  int64_t grid = ((n_items + kWaves - 1) / kWaves);
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (attr != hipSuccess) return attr;
+  int64_t grid = (items + kWaves - 1) / kWaves;
   if (grid > num_cu) grid = num_cu;  // persistent: one workgroup per CU
-  // whole 4-column groups of a row go out in one store when the rows are
-  // aligned for it and the output's byte extent fits 32-bit offsets
-  const int es = y_dtype == 0 ? 4 : 2;
-  const int64_t extent = total_m > 0 ? ((total_m - 1) * ld_y + N) * es : 0;
-  const bool aligned = (reinterpret_cast<uintptr_t>(y) % (4 * es)) == 0 && ld_y % 4 == 0;
-  const uint32_t y_bytes = aligned && extent < (int64_t)0xFFFFFFF0 ? (uint32_t)extent : 0u;
-  Shape sh{(int)N, (int)(K / kJobK), (int)tiles, (int)n_items, (int)grid * kWaves, total_m,
-           row_index != nullptr ? a_rows : total_m, y_bytes};
-  kern<<<(unsigned)grid, kThreads, smem, stream>>>(sh, m_offsets, row_index, (int)K, a.q, a.s, a.g,
-                                                   b.q, b.s, b.g, y, y_dtype, ld_y);
+  ps.count = count;
+  ps.n_items = (int)items;
+  ps.stride = (int)grid * kWaves;
+  gemm_grouped_kernel<<<(unsigned)grid, kThreads, smem, stream>>>(ps);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
+                               int64_t total_m, int64_t a_rows, int64_t N, int64_t K,
+                               PackedOperand a, PackedOperand b, void* y, int y_dtype,
+                               int64_t ld_y, hipStream_t stream) {
+  const GroupedProblem g{G, m_offsets, row_index, total_m, a_rows, N, K, a, b, y, y_dtype, ld_y};
+  return launch_gemm_grouped_multi(1, &g, stream);
 }
 
 }  // namespace nvfp4

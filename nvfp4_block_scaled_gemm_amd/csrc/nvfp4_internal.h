@@ -71,6 +71,24 @@ hipError_t launch_gemm_decode(int64_t M, int64_t N, int64_t K, PackedOperand a,
                               PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                               hipStream_t stream, QuantOut qo = {});
 
+// One grouped GEMM of a launch (row_index as above; a_rows is used only with
+// a row_index).
+struct GroupedProblem {
+  int32_t G;
+  const int32_t* m_offsets;
+  const int32_t* row_index;
+  int64_t total_m, a_rows, N, K;
+  PackedOperand a, b;
+  void* y;
+  int y_dtype;
+  int64_t ld_y;
+};
+constexpr int kGroupedMaxProblems = 4;  // = NVFP4_GROUPED_MAX_PROBLEMS
+
+// gemm_grouped.hip: 1..kGroupedMaxProblems problems in one persistent launch,
+// each with K % 512 == 0 and operands < 4 GiB.
+hipError_t launch_gemm_grouped_multi(int count, const GroupedProblem* probs, hipStream_t stream);
+
 // gemm_grouped.hip: K % 512 == 0, operands < 4 GiB; row_index as above.
 hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
                                int64_t total_m, int64_t a_rows, int64_t N, int64_t K,

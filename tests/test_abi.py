@@ -285,3 +285,50 @@ def test_quantize_noalloc_validation(kw, status):
                                           args["ld_x"], args["q"], args["s"],
                                           args["global_scale"], args["flags"], None)
     assert st == status
+
+
+def _gp(**kw):
+    args = dict(G=4, m_offsets=0x10000, row_index=None, total_m=8, a_rows=0, N=8, K=128,
+                a_q=0x10000, a_s=0x10000, a_g=0x10000, b_q=0x10000, b_s=0x10000, b_g=0x10000,
+                y=0x10000, y_dtype=nv.NVFP4_BF16, ld_y=8)
+    args.update(kw)
+    return nv.GroupedProblem(**args)
+
+
+def _multi(probs, count=None):
+    arr = (nv.GroupedProblem * max(len(probs), 1))(*probs)
+    return nv.load().nvfp4_grouped_gemm_multi(len(probs) if count is None else count, arr, None)
+
+
+def test_grouped_problem_struct_layout():
+    """The ctypes mirror of nvfp4_grouped_problem has the C layout (x86-64:
+    int32 G padded to 8, then pointers and int64s, int y_dtype padded)."""
+    assert ctypes.sizeof(nv.GroupedProblem) == 128
+    assert nv.GroupedProblem.m_offsets.offset == 8
+    assert nv.GroupedProblem.y_dtype.offset == 112
+    assert nv.GroupedProblem.ld_y.offset == 120
+
+
+@pytest.mark.parametrize("probs,count,status", [
+    ([], None, nv.NVFP4_OK),
+    ([_gp()], -1, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp()] * 5, None, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp(K=40)], None, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp(total_m=0), _gp(K=40)], None, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp(total_m=0), _gp(m_offsets=None)], None, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp(total_m=0), _gp(a_rows=5)], None, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp(row_index=0x10000, a_rows=-1)], None, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp(row_index=0x10000, a_rows=1 << 31)], None, nv.NVFP4_ERR_UNSUPPORTED),
+    ([_gp(total_m=0), _gp(N=0, ld_y=0), _gp(G=0, total_m=0)], None, nv.NVFP4_OK),
+    ([_gp(total_m=0), _gp(ld_y=4)], None, nv.NVFP4_ERR_INVALID_ARG),
+    ([_gp(total_m=0), _gp(y_dtype=7)], None, nv.NVFP4_ERR_INVALID_ARG),
+])
+def test_grouped_multi_argument_checks(probs, count, status):
+    """Every problem is validated before anything is enqueued: an invalid
+    one anywhere in the list fails the call; empty problems are skipped."""
+    assert _multi(probs, count) == status
+
+
+def test_grouped_multi_null_problem_list():
+    assert nv.load().nvfp4_grouped_gemm_multi(1, None, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert nv.load().nvfp4_grouped_gemm_multi(0, None, None) == nv.NVFP4_OK
