@@ -53,12 +53,13 @@ int grouped_check(int32_t G, const int32_t* m_offsets, int64_t total_m, int64_t 
   return NVFP4_OK;
 }
 
-// The streaming grouped kernel takes K % 512 == 0, aligned rows and
-// operands whose byte offsets fit 32 bits; anything else runs the general
-// kernel.
+// The streaming grouped kernel takes K % 512 == 0, aligned rows, operands
+// whose byte offsets fit 32 bits and unit counts that fit 32-bit ints;
+// anything else runs the general kernel.
 bool grouped_streams(const nvfp4::GroupedProblem& g) {
   return g.K > 0 && tiled_ok(g.K, g.a.q, g.a.s, 512) && tiled_ok(g.K, g.b.q, g.b.s, 512) &&
-         offsets32_ok(g.total_m, g.K) && offsets32_ok(g.a_rows, g.K) && offsets32_ok(g.N, g.K);
+         offsets32_ok(g.total_m, g.K) && offsets32_ok(g.a_rows, g.K) && offsets32_ok(g.N, g.K) &&
+         nvfp4::grouped_units_fit(g.G, g.total_m, g.N);
 }
 
 int grouped_run(const nvfp4::GroupedProblem& g, hipStream_t st) {

@@ -80,6 +80,12 @@ constexpr int kLoadsPerJob = kNibLoads + kScLoads + 10;  // memory instructions 
 static_assert(kFrags % 2 == 0, "scale DMAs cover 32 rows");
 constexpr uint32_t kOob = 0xFFFFFFF0u;           // offset past every operand (reads zero)
 constexpr int kMaxProblems = kGroupedMaxProblems;
+constexpr int kPrefix = 1024;                    // prefix entries per problem (LDS)
+constexpr int kMaxGroups = kPrefix - 1;          // experts per problem of one launch
+constexpr int kXcds = 8;                         // XCDs the workgroups go round-robin over
+constexpr int kLds = kWaves * kWaveLds + kMaxProblems * kPrefix * 4;
+static_assert(kLds <= 160 * 1024, "LDS budget");
+static_assert(kPrefix % kThreads == 0, "experts per thread");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -115,8 +121,7 @@ struct Problem {
   int64_t ld_y;
   int64_t total_m;
   int64_t a_rows;            // rows of the activation operand
-  int N, K, nunits, tiles;
-  int item_base, n_items;    // the problem's items: [item_base, item_base + n_items)
+  int G, N, K, nunits, tiles;
   int y_dtype;
   uint32_t y_bytes;          // extent of y when below 4 GiB and its rows take
                              // 8-byte (bf16) / 16-byte (fp32) stores, else 0
@@ -124,7 +129,7 @@ struct Problem {
 
 struct Problems {
   Problem p[kMaxProblems];
-  int count, n_items, stride;  // problems, items of all of them, grid stride
+  int count;
 };
 
 // The launch's problem list is its only argument, so it starts the
@@ -148,62 +153,125 @@ __device__ __forceinline__ const T __attribute__((address_space(4)))* scalar_ptr
   return (const T __attribute__((address_space(4)))*)p;
 }
 
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Token rows [r0, r1) of expert e, clamped into [0, total_m) whatever the
+// offsets hold.
+template <typename Ptr>
+__device__ __forceinline__ void expert_rows(Ptr m_offsets, int64_t total_m, int e, int64_t& r0,
+                                            int64_t& r1) {
+  int64_t a = m_offsets[e], b = m_offsets[e + 1];
+  a = a < 0 ? 0 : (a > total_m ? total_m : a);
+  b = b < a ? a : (b > total_m ? total_m : b);
+  r0 = a;
+  r1 = b;
+}
+
+// Work units.  Expert e with r_e token rows has C_e = ceil(r_e / 32)
+// chunks of up to 32 tokens; a unit is (expert, 64-row weight tile,
+// chunk), and a wave runs it over all of K.  Units are numbered expert by
+// expert, tile by tile, chunk fastest, so expert e owns units
+// [tiles * pp[e], tiles * pp[e + 1]) where pp is the prefix sum of C_e.
+// Every workgroup builds pp for each problem in LDS at start (four experts
+// per thread, a wave scan and a scan of the wave totals); experts without
+// tokens own no units.
+__device__ __forceinline__ void build_prefixes(const Problems& ps, int* pref, int* tmp) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int pi = 0; pi < ps.count; ++pi) {
+    ProblemRef P = problem(pi);
+    const int G = P.G;
+    int* pp = pref + pi * kPrefix;
+    int c[kPrefix / kThreads], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPrefix / kThreads; ++j) {
+      const int e = (kPrefix / kThreads) * t + j;
+      int n = 0;
+      if (e < G) {
+        int64_t r0, r1;
+        expert_rows(P.m_offsets, P.total_m, e, r0, r1);
+        n = (int)((r1 - r0 + 31) / 32);
+      }
+      sum += n;
+      c[j] = sum;
+    }
+    int v = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(v, d, 64);
+      v += lane >= d ? y : 0;
+    }
+    if (lane == 63) tmp[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += tmp[w];
+    const int excl = before + v - sum;
+#pragma unroll
+    for (int j = 0; j < kPrefix / kThreads; ++j) {
+      const int e = (kPrefix / kThreads) * t + j;
+      if (e < G) pp[e + 1] = excl + c[j];
+    }
+    if (t == 0) pp[0] = 0;
+    __syncthreads();  // pp complete; tmp free for the next problem
+  }
+}
+
+// Largest e in [0, G) with pp[e] <= key, all 64 lanes searching at once
+// (pp[0] = 0 <= key, and G <= kPrefix - 1 so every read stays inside the
+// problem's prefix array).
+__device__ __forceinline__ int find_expert(const int* pp, int G, int key, int lane) {
+  int lo = 0;
+  if (G > 64) {  // uniform: 64 segments of 16 experts, then one segment
+    const int i = lane * 16;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(i < G && pp[i] <= key);
+    lo = (63 - __builtin_clzll(m)) * 16;
+    const int j = min(lo + lane, kPrefix - 1);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < 16 && j < G && pp[j] <= key);
+    return uniform(lo + 63 - __builtin_clzll(m2));
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(lane < G && pp[lane] <= key);
+  return uniform(63 - __builtin_clzll(m));
+}
+
 // A wave's position in its job sequence over one problem (all fields
 // wave-uniform).
 struct Cursor {
-  int item;              // item of the problem (>= n_items: finished)
-  int e, n0;             // expert and first weight row of the item
-  int r0, r1;            // the expert's token rows [r0, r1)
-  int c0;                // first token row of the current chunk
-  int u;                 // current K slice (job) of kJobK elements
-  int rows_c0;           // chunk whose activation rows xq / xs hold (-1: none)
+  int u;                 // unit of the problem (>= units: finished)
+  int e, n0;             // expert and first weight row of the unit
+  int c0, r1;            // the unit's token rows [c0, r1), at most 32
+  int k;                 // current K slice (job) of kJobK elements
   uint32_t xq[2], xs[2]; // this lane's activation row offsets per token
                          // fragment (kOob: no row)
 };
 
-// Expert rows of item `it`, clamped into [0, total_m) whatever the offsets
-// hold.  The expert index is made explicitly scalar so the two offsets come
-// in through the scalar cache (their wait never drains the vector loads).
-__device__ __forceinline__ void item_rows(ProblemRef P, int it, Cursor& c) {
-  c.item = it;
-  c.e = __builtin_amdgcn_readfirstlane(it / P.tiles);
-  c.n0 = (it - c.e * P.tiles) * kRows;
-  const auto m_offsets = scalar_ptr(P.m_offsets);
-  int64_t a = m_offsets[c.e], b = m_offsets[c.e + 1];
-  a = a < 0 ? 0 : (a > P.total_m ? P.total_m : a);
-  b = b < a ? a : (b > P.total_m ? P.total_m : b);
-  c.r0 = (int)a;
-  c.r1 = (int)b;
-}
-
-// First item at or after `it` (stepping by the grid stride) with tokens.
-// Both exits store the same fields, so the cursor stays in registers.
-__device__ __forceinline__ void seek_item(ProblemRef P, int it, int stride, Cursor& c) {
-  const int n_items = P.n_items;
-  bool found = false;
-  for (; it < n_items; it += stride) {
-    item_rows(P, it, c);
-    if (c.r1 > c.r0) {
-      found = true;
-      break;
+// Unit u of the problem (or the finished state past the last one).  Every
+// field is stored once, on both paths, so the cursor stays in registers.
+__device__ __forceinline__ void decode(ProblemRef P, const int* pp, int units, int u, int lane,
+                                       Cursor& c) {
+  int cu = units, e = 0, n0 = 0, c0 = 0, r1 = 0;
+  if (u < units) {
+    const int tiles = P.tiles;
+    e = find_expert(pp, P.G, u / tiles, lane);
+    const int p0 = uniform(pp[e]), ce = uniform(pp[e + 1]) - p0;
+    if (ce > 0) {  // always, unless the offsets were inconsistent
+      const int local = u - tiles * p0;
+      const int t = min(max(local / ce, 0), tiles - 1), ch = local - t * ce;
+      int64_t er0, er1;
+      expert_rows(scalar_ptr(P.m_offsets), P.total_m, e, er0, er1);
+      // rows stay inside the expert's clamped range whatever pp holds
+      int64_t lo = er0 + 32 * (int64_t)ch;
+      lo = lo < er0 ? er0 : (lo > er1 ? er1 : lo);
+      cu = u;
+      n0 = t * kRows;
+      c0 = (int)lo;
+      r1 = (int)(er1 < lo + 32 ? er1 : lo + 32);
     }
   }
-  if (!found) {
-    c.item = n_items;
-    c.e = c.n0 = c.r0 = c.r1 = 0;
-  }
-  c.c0 = c.r0;
-  c.u = 0;
-  c.rows_c0 = -1;
-}
-
-__device__ __forceinline__ void advance(ProblemRef P, int stride, Cursor& c) {
-  if (c.item >= P.n_items) return;
-  if (++c.u < P.nunits) return;
-  c.u = 0;
-  c.c0 += 32;
-  if (c.c0 < c.r1) return;
-  seek_item(P, c.item + stride, stride, c);
+  c.u = cu;
+  c.e = e;
+  c.n0 = n0;
+  c.c0 = c0;
+  c.r1 = r1;
+  c.k = 0;
 }
 
 __device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
@@ -213,13 +281,13 @@ struct XFrags {
   u32x2 s[2];     // their 8 scale bytes
 };
 
-// The items of problem pi that fall to wave `w` of the grid (global item
-// ids w, w + stride, ...), through its own load/compute pipeline.  GATHER
-// (the problem has a routing index): grouped row r reads activation row
-// row_index[r] (an index outside [0, a_rows) reads as a zero row);
-// otherwise grouped row r is activation row r.
+// The units [first, first + stride, ...) of problem pi, through its own
+// load/compute pipeline.  GATHER (the problem has a routing index): grouped
+// row r reads activation row row_index[r] (an index outside [0, a_rows)
+// reads as a zero row); otherwise grouped row r is activation row r.
 template <bool GATHER>
-__device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* ring) {
+__device__ __forceinline__ void run_problem(int pi, const int* pp, int units, int first,
+                                            int stride, uint8_t* ring) {
   ProblemRef P = problem(pi);
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, lq = lane >> 4;
@@ -232,12 +300,12 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
   const auto row_index = scalar_ptr(P.row_index);  // used with GATHER
 
   // Load offsets = a per-lane constant + a scalar per job.  Weight nibble
-  // load k (16 B per lane) covers item rows 4k .. 4k+3: lane L takes row
+  // load k (16 B per lane) covers unit rows 4k .. 4k+3: lane L takes row
   // 4k + L/16 and physical 16-byte chunk L%16 of its 256-byte LDS row, which
   // holds logical chunk (L%16) ^ (row%16).  The scale load covers all 32 rows
   // (lane L: row L/2, half L%2).  Token fragment g holds chunk rows 16g+li.
   // Offsets stay in the range-checked vector operand, so weight rows past N
-  // read as zero; token rows outside the expert's chunk get an out-of-range
+  // read as zero; token rows outside the unit's chunk get an out-of-range
   // offset (zero, and no memory traffic).
   uint32_t wq_lane[kNibLoads];
 #pragma unroll
@@ -247,15 +315,14 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
   }
   const uint32_t ws_lane = (uint32_t)(lane >> 1) * srow + (uint32_t)(lane & 1) * 16u;
 
-  // Activation rows of the chunk at c.c0 for this lane's two token
-  // fragments (chunk rows 16g + li), as byte offsets of the row starts.
-  // With a routing index the chunk's 32 indices come through the scalar
-  // cache (so their wait never drains the vector loads) and each lane picks
-  // its own.
+  // Activation rows of the unit's chunk for this lane's two token fragments
+  // (chunk rows 16g + li), as byte offsets of the row starts.  With a
+  // routing index the chunk's 32 indices come through the scalar cache (so
+  // their wait never drains the vector loads) and each lane picks its own.
   auto chunk_rows = [&](Cursor& c) {
     int src[2] = {c.c0 + li, c.c0 + 16 + li};
     if constexpr (GATHER) {
-      const int base = __builtin_amdgcn_readfirstlane(c.c0);
+      const int base = uniform(c.c0);
       const int last = (int)P.total_m - 1;
       int v0 = 0, v1 = 0;
 #pragma unroll
@@ -273,7 +340,12 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
       c.xq[g] = ok ? (uint32_t)src[g] * qrow : kOob;
       c.xs[g] = ok ? (uint32_t)src[g] * srow : kOob;
     }
-    c.rows_c0 = c.c0;
+  };
+
+  auto advance = [&](Cursor& c) {
+    if (c.u >= units) return;
+    if (++c.k < P.nunits) return;
+    decode(P, pp, units, c.u < units - stride ? c.u + stride : units, lane, c);
   };
 
   XFrags xs[kSlots];
@@ -283,19 +355,19 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
   // pads with loads of expert 0's first slice.
   auto issue = [&](Cursor& c, auto sc) {
     constexpr int S = decltype(sc)::value;
-    const bool live = c.item < P.n_items;
-    if (live && c.rows_c0 != c.c0) chunk_rows(c);  // uniform
+    const bool live = c.u < units;
+    if (live && c.k == 0) chunk_rows(c);  // uniform
     const int e = live ? c.e : 0;
     const uint8_t* wq = P.b_q + (int64_t)e * P.N * qrow;
     const uint8_t* ws = P.b_s + (int64_t)e * P.N * srow;
-    const uint32_t wq_job = live ? (uint32_t)c.n0 * qrow + (uint32_t)c.u * kRowNib : 0u;
-    const uint32_t ws_job = live ? (uint32_t)c.n0 * srow + (uint32_t)c.u * kRowSc : 0u;
-    const uint32_t xq_job = (uint32_t)c.u * kRowNib + (uint32_t)lq * 64u;
-    const uint32_t xs_job = (uint32_t)c.u * kRowSc + (uint32_t)lq * 8u;
+    const uint32_t wq_job = live ? (uint32_t)c.n0 * qrow + (uint32_t)c.k * kRowNib : 0u;
+    const uint32_t ws_job = live ? (uint32_t)c.n0 * srow + (uint32_t)c.k * kRowSc : 0u;
+    const uint32_t xq_job = (uint32_t)c.k * kRowNib + (uint32_t)lq * 64u;
+    const uint32_t xs_job = (uint32_t)c.k * kRowSc + (uint32_t)lq * 8u;
     uint8_t* slot = ring + S * kSlotBytes;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      // token rows outside the expert's chunk are not fetched at all
+      // token rows outside the unit's chunk are not fetched at all
       const bool ok = live && c.xq[g] != kOob;
       const uint32_t qo = ok ? c.xq[g] + xq_job : kOob;
 #pragma unroll
@@ -315,8 +387,8 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
 #pragma unroll
     for (int g = 0; g < 2; ++g) acc[f][g] = f32x4{0, 0, 0, 0};
 
-  // One job from slot S (its loads have landed), then the item-chunk
-  // epilogue if this was its last slice.
+  // One job from slot S (its loads have landed), then the unit's epilogue
+  // if this was its last slice.
   auto compute = [&](const Cursor& c, auto sc) {
     constexpr int S = decltype(sc)::value;
     const uint8_t* slot = ring + S * kSlotBytes;
@@ -333,7 +405,7 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
       sw[f][1] = to_scales(s8[1]);
     }
     const Scales sx0[2] = {to_scales(xs[S].s[0][0]), to_scales(xs[S].s[0][1])};
-    const int ntok = min(32, c.r1 - c.c0);
+    const int ntok = c.r1 - c.c0;
     // step T (0..15) uses dword T of the lane's 64 bytes: block T/2, i.e.
     // scale pair word T/8, block (T/2) % 4 within it
     if (ntok > 16) {  // wave-uniform
@@ -371,7 +443,7 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    if (c.u == P.nunits - 1) {
+    if (c.k == P.nunits - 1) {
       // acc[f][g] reg r: weight row n0 + 16f + 4*lq + r, token c0 + 16g + li
       const float alpha = scalar_ptr(P.a_g)[0] * scalar_ptr(P.b_g)[c.e];
       void* __restrict__ y = P.y;
@@ -418,17 +490,13 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
     }
   };
 
-  // the problem's first item with global id = w modulo the grid stride
-  int first = (w - P.item_base) % stride;
-  first += first < 0 ? stride : 0;
   Cursor lc, cc;
-  lc.rows_c0 = -1;
-  seek_item(P, first, stride, lc);
+  decode(P, pp, units, first, lane, lc);
+  if (lc.u >= units) return;  // nothing of this problem for the wave
   cc = lc;
-  if (cc.item >= P.n_items) return;  // nothing of this problem for the wave
   static_for<kSlots - 1>([&](auto sc) {
     issue(lc, sc);
-    advance(P, stride, lc);
+    advance(lc);
   });
   // jobs rotate through the slots; the loads of job j + kSlots - 1 go out
   // before job j waits for its own (the younger jobs may stay in flight)
@@ -438,33 +506,59 @@ __device__ __forceinline__ void run_problem(int pi, int w, int stride, uint8_t* 
       constexpr int S = decltype(sc)::value;
       if (!more) return;
       issue(lc, std::integral_constant<int, (S + kSlots - 1) % kSlots>{});
-      advance(P, stride, lc);
+      advance(lc);
       wait_vmcnt<(kSlots - 1) * kLoadsPerJob>();
       compute(cc, sc);
-      advance(P, stride, cc);
-      more = cc.item < P.n_items;
+      advance(cc);
+      more = cc.u < units;
     });
   }
   wait_vmcnt<0>();  // padding loads land before the next problem reuses the ring
 }
 
-// The waves of the grid walk the union of the problems' items with a fixed
+// The waves of the grid walk the union of the problems' units with a fixed
 // stride, problem by problem; each problem runs its own pipeline (drained
 // between problems), so its operand descriptors stay in scalar registers.
+// Waves are numbered XCD by XCD (workgroups go round-robin over the XCDs),
+// so consecutive units -- the chunks of one weight tile -- run at the same
+// time on one XCD and share its L2 for that tile.
 __global__ __launch_bounds__(kThreads, kWaves / 4) void gemm_grouped_kernel(const Problems ps) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = uniform(threadIdx.x >> 6);
+  int* const pref = reinterpret_cast<int*>(smem + kWaves * kWaveLds);
+  build_prefixes(ps, pref, reinterpret_cast<int*>(smem));
+  const int grid = gridDim.x, b = blockIdx.x;
+  const int x = b % kXcds, i = b / kXcds;
+  const int v = (x * (grid / kXcds) + min(x, grid % kXcds) + i) * kWaves + wave;
+  const int stride = grid * kWaves;
   uint8_t* ring = smem + wave * kWaveLds;
-  const int w = blockIdx.x * kWaves + wave;
+  int base = 0;  // first global unit of problem pi
   for (int pi = 0; pi < ps.count; ++pi) {
-    if (problem(pi).row_index != nullptr)  // uniform
-      run_problem<true>(pi, w, ps.stride, ring);
+    ProblemRef P = problem(pi);
+    const int* pp = pref + pi * kPrefix;
+    const int units = P.tiles * uniform(pp[P.G]);
+    int first = (v - base) % stride;
+    first += first < 0 ? stride : 0;
+    if (P.row_index != nullptr)  // uniform
+      run_problem<true>(pi, pp, units, first, stride, ring);
     else
-      run_problem<false>(pi, w, ps.stride, ring);
+      run_problem<false>(pi, pp, units, first, stride, ring);
+    base += units;
   }
 }
 
+// Upper bound of a problem's units: each expert with tokens adds at most
+// one partial chunk.
+int64_t unit_bound(int64_t G, int64_t total_m, int64_t N) {
+  const int64_t tiles = (N + kRows - 1) / kRows;
+  return tiles * ((G < total_m ? G : total_m) + (total_m + 31) / 32);
+}
+
 }  // namespace
+
+bool grouped_units_fit(int64_t G, int64_t total_m, int64_t N) {
+  return unit_bound(G, total_m, N) < ((int64_t)1 << 29);
+}
 
 hipError_t launch_gemm_grouped_multi(int count, const GroupedProblem* probs, hipStream_t stream) {
   if (count < 1 || count > kMaxProblems) return hipErrorInvalidValue;
@@ -476,37 +570,49 @@ hipError_t launch_gemm_grouped_multi(int count, const GroupedProblem* probs, hip
       n = 256;
     num_cu = n;
   }
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (attr != hipSuccess) return attr;
+  // Problems with more than kMaxGroups experts run as pieces of consecutive
+  // experts (each piece reads only its own experts' rows); up to
+  // kMaxProblems pieces go into one launch.
   Problems ps{};
-  int64_t items = 0;
+  int64_t bound = 0;
+  auto flush = [&]() -> hipError_t {
+    if (ps.count == 0) return hipSuccess;
+    int64_t grid = (bound + kWaves - 1) / kWaves;
+    if (grid > num_cu) grid = num_cu;  // persistent: one workgroup per CU
+    if (grid < 1) grid = 1;
+    gemm_grouped_kernel<<<(unsigned)grid, kThreads, kLds, stream>>>(ps);
+    ps = Problems{};
+    bound = 0;
+    return hipGetLastError();
+  };
   for (int i = 0; i < count; ++i) {
     const GroupedProblem& g = probs[i];
-    Problem& P = ps.p[i];
+    if (!grouped_units_fit(g.G, g.total_m, g.N)) return hipErrorInvalidValue;
     const int64_t tiles = (g.N + kRows - 1) / kRows;
-    const int64_t n_items = tiles * g.G;
     // whole 4-column groups of a row go out in one store when the rows are
     // aligned for it and the output's byte extent fits 32-bit offsets
     const int es = g.y_dtype == 0 ? 4 : 2;
     const int64_t extent = g.total_m > 0 ? ((g.total_m - 1) * g.ld_y + g.N) * es : 0;
     const bool aligned = (reinterpret_cast<uintptr_t>(g.y) % (4 * es)) == 0 && g.ld_y % 4 == 0;
-    P = Problem{g.m_offsets, g.row_index, g.a.q, g.a.s, g.a.g, g.b.q, g.b.s, g.b.g, g.y, g.ld_y,
-                g.total_m, g.row_index != nullptr ? g.a_rows : g.total_m, (int)g.N, (int)g.K,
-                (int)(g.K / kJobK), (int)tiles, (int)items, (int)n_items, g.y_dtype,
-                aligned && extent < (int64_t)0xFFFFFFF0 ? (uint32_t)extent : 0u};
-    items += n_items;
-    if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const uint32_t y_bytes = aligned && extent < (int64_t)0xFFFFFFF0 ? (uint32_t)extent : 0u;
+    for (int64_t g0 = 0; g0 < g.G; g0 += kMaxGroups) {
+      const int64_t ng = g.G - g0 < kMaxGroups ? g.G - g0 : kMaxGroups;
+      if (ps.count == kMaxProblems) {
+        const hipError_t err = flush();
+        if (err != hipSuccess) return err;
+      }
+      ps.p[ps.count++] = Problem{
+          g.m_offsets + g0, g.row_index, g.a.q, g.a.s, g.a.g,
+          g.b.q + g0 * g.N * (g.K / 2), g.b.s + g0 * g.N * (g.K / 16), g.b.g + g0, g.y, g.ld_y,
+          g.total_m, g.row_index != nullptr ? g.a_rows : g.total_m, (int)ng, (int)g.N, (int)g.K,
+          (int)(g.K / kJobK), (int)tiles, g.y_dtype, y_bytes};
+      bound += unit_bound(ng, g.total_m, g.N);
+    }
   }
-  if (items == 0) return hipSuccess;
-  const int smem = kWaves * kWaveLds;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-  if (attr != hipSuccess) return attr;
-  int64_t grid = (items + kWaves - 1) / kWaves;
-  if (grid > num_cu) grid = num_cu;  // persistent: one workgroup per CU
-  ps.count = count;
-  ps.n_items = (int)items;
-  ps.stride = (int)grid * kWaves;
-  gemm_grouped_kernel<<<(unsigned)grid, kThreads, smem, stream>>>(ps);
-  return hipGetLastError();
+  return flush();
 }
 
 hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,

@@ -88,6 +88,9 @@ constexpr int kGroupedMaxProblems = 4;  // = NVFP4_GROUPED_MAX_PROBLEMS
 // gemm_grouped.hip: 1..kGroupedMaxProblems problems in one persistent launch,
 // each with K % 512 == 0 and operands < 4 GiB.
 hipError_t launch_gemm_grouped_multi(int count, const GroupedProblem* probs, hipStream_t stream);
+// The streaming grouped kernel numbers its work units with 32-bit ints:
+// true when a problem of this size fits.
+bool grouped_units_fit(int64_t G, int64_t total_m, int64_t N);
 
 // gemm_grouped.hip: K % 512 == 0, operands < 4 GiB; row_index as above.
 hipError_t launch_gemm_grouped(int32_t G, const int32_t* m_offsets, const int32_t* row_index,
