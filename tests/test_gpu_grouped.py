@@ -326,3 +326,38 @@ def test_general_kernel_past_its_row_chunks():
                               row_index=t(idx.astype(np.int32)))
     torch.cuda.synchronize()
     check(y, idx[rows])
+
+
+def test_more_experts_than_one_launch_piece():
+    """2500 experts (one launch handles at most 1023 per problem, so the
+    call runs pieces of consecutive experts), most with 0-3 rows and one
+    with 70, through the streaming kernel (K = 512)."""
+    rng = np.random.default_rng(2500)
+    counts = (rng.integers(0, 4, size=2500) * (rng.random(2500) < 0.6)).tolist()
+    counts[1700] = 70
+    _run(counts, 64, 512, "f32", seed=2500)
+
+
+@pytest.mark.parametrize("K", [512, 48])
+def test_inconsistent_offsets_stay_inside_the_output(K):
+    """Offsets that decrease and overlap (a violated precondition): the
+    result is unspecified, but nothing outside y's rows [0, total_m) may be
+    written and the call must finish.  K = 512 runs the streaming kernel,
+    K = 48 the general one."""
+    need_gpu()
+    rng = np.random.default_rng(K)
+    N, total = 72, 60
+    off = torch.tensor([0, 50, 10, 70, -5, 60], dtype=torch.int32)
+    G = len(off) - 1
+    aq, as_ = _rand_packed(rng, (total,), K)
+    bq, bs = _rand_packed(rng, (G, N), K)
+    dev = "cuda"
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)  # noqa: E731
+    buf = torch.full((total + 8, N), -7.0, dtype=torch.float32, device=dev)
+    y = buf[4:4 + total]
+    note(f"grouped inconsistent offsets K={K}")
+    nv.nvfp4_grouped_gemm(off.to(dev), total, (t(aq), t(as_), torch.ones(1, device=dev)),
+                          (t(bq), t(bs), torch.ones(G, device=dev)), out_dtype="f32", y=y)
+    torch.cuda.synchronize()
+    full = buf.cpu().numpy()
+    assert np.all(full[:4] == -7.0) and np.all(full[4 + total:] == -7.0)
