@@ -131,3 +131,48 @@ def test_side_stream_without_context_static_scale():
     assert torch.equal(ref_y, got_y)
     for r, g in zip(ref_o, got_o):
         assert torch.equal(r, g)
+
+
+def test_graph_decode_kernels_and_grouped_multi():
+    """The decode kernels (1, 4, 16 and 32 tokens at K = 8192: the
+    whole-row and LDS-ring weight streams) and a two-problem grouped launch
+    captured into one graph; every replay reproduces the eager results."""
+    need_gpu()
+    dev = "cuda"
+    w = nv.nvfp4_quantize(wl.randn((1024, 8192), 21, "bf16").to(dev))
+    xs = {m: nv.nvfp4_quantize(wl.randn((m, 8192), 22 + m, "bf16").to(dev)) for m in (1, 4, 16, 32)}
+    ys = {m: torch.empty((m, 1024), dtype=torch.bfloat16, device=dev) for m in xs}
+    counts = [5, 0, 40, 3]
+    off = wl.ragged_offsets(counts).to(dev)
+    total = sum(counts)
+    wg = nv.nvfp4_quantize(wl.randn((4 * 256, 1024), 30, "bf16").to(dev))
+    bw = (wg[0].view(4, 256, 512), wg[1].view(4, 256, 64), wg[2].repeat(4))
+    a = nv.nvfp4_quantize(wl.randn((64, 1024), 31, "bf16").to(dev))
+    idx = torch.from_numpy(np.random.default_rng(3).integers(0, 64, total).astype(np.int32)).to(dev)
+    a2 = nv.nvfp4_quantize(wl.randn((total, 1024), 32, "bf16").to(dev))
+    yg = [torch.empty((total, 256), dtype=torch.float32, device=dev) for _ in range(2)]
+    calls = [dict(m_offsets=off, total_m=total, a=a, b=bw, out_dtype="f32", y=yg[0], row_index=idx),
+             dict(m_offsets=off, total_m=total, a=a2, b=bw, out_dtype="f32", y=yg[1])]
+
+    def step():
+        for m in xs:
+            nv.nvfp4_gemm(xs[m], w, "bf16", y=ys[m])
+        nv.nvfp4_grouped_gemm_multi(calls)
+
+    outs = [*ys.values(), *yg]
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    note("capture decode GEMMs and a grouped launch")
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(3)
+        torch.cuda.synchronize()
+        note(f"decode graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for r, got in zip(ref, outs):
+            assert torch.equal(r, got), f"replay {rep} differs"
