@@ -9,3 +9,6 @@ from .nvfp4_ref import (  # noqa: F401
     global_scale_ref, grouped_gemm_ref, pack_nibbles, quantize_ref,
     tolerance, ulp_bf16, unpack_nibbles,
 )
+from .mxfp4_ref import (  # noqa: F401
+    MX_BLOCK, e8m0_decode, mxfp4_dequantize_ref, mxfp4_gemm_ref, mxfp4_quantize_ref,
+)

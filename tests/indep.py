@@ -121,3 +121,48 @@ def indep_dequant_f64(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     sv = torch.from_numpy(np.ascontiguousarray(s)).view(torch.float8_e4m3fn)
     sv = sv.to(torch.float64).numpy()
     return e2 * np.repeat(sv, 16, axis=1)
+
+
+def e8m0_fraction(code: int) -> Fraction:
+    """Exact value of an E8M0 byte, taken from torch's float8_e8m0fnu decoder."""
+    t = torch.tensor([code & 0xFF], dtype=torch.uint8).view(torch.float8_e8m0fnu)
+    v = float(t.to(torch.float64).item())
+    if v != v:
+        raise ValueError("NaN code")
+    return Fraction(v)
+
+
+def mx_shared_exponent_bruteforce(amax: Fraction) -> int:
+    """Largest E with 2^E <= amax (found by exact comparisons), minus the
+    exponent of E2M1's largest value (6 = 1.5 * 2^2), clamped to
+    [-127, 127]; -127 for a zero block."""
+    if amax == 0:
+        return -127
+    e = 0
+    while Fraction(2) ** e > amax:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= amax:
+        e += 1
+    return max(-127, min(127, e - 2))
+
+
+def mx_quantize_bruteforce(x: np.ndarray):
+    """Exact-rational MXFP4 conversion of finite values: per 32-element
+    block the shared exponent above, each element the nearest grid value
+    E2M1 * 2^E by distance (ties to the even code; beyond 6 * 2^E the
+    nearest is 6 * 2^E).  Returns (nibbles [rows, K] int, scale bytes
+    [rows, K/32] int)."""
+    rows, cols = x.shape
+    nib = np.zeros((rows, cols), dtype=np.int64)
+    sc = np.zeros((rows, cols // 32), dtype=np.int64)
+    for r in range(rows):
+        for b in range(cols // 32):
+            vals = [Fraction(float(v)) for v in x[r, 32 * b:32 * b + 32]]
+            E = mx_shared_exponent_bruteforce(max(abs(v) for v in vals))
+            sc[r, b] = E + 127
+            grid = [g * Fraction(2) ** E for g in E2M1_POS]
+            for i, v in enumerate(vals):
+                code = nearest_even(abs(v), grid)
+                sign = 1 if np.signbit(x[r, 32 * b + i]) else 0
+                nib[r, 32 * b + i] = (sign << 3) | code
+    return nib, sc
