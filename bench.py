@@ -26,6 +26,8 @@ M = N = K = 16384 outlier workload (quantiser on x alone, then the GEMM);
 ``library_reference`` torch's bf16 GEMM at the linear shape and a 1 GiB
 device copy on the same box, as context for what the hardware gives a
 plain dense GEMM and a plain stream.
+``mxfp4`` the MXFP4 variant (32-element E8M0 blocks) at the linear shape
+against the dense FP4 peak.
 ``cpu_baseline`` times the CPU oracle on a bounded row slice of the same step.
 """
 from __future__ import annotations
@@ -42,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 (and FP6) matrix-core peak
 PREWARM_S = 1.0               # untimed back-to-back steps before timing
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_linear_m4096_n8192_k8192.json")
 GEMM_SOURCES = ["gemm_mfma.hip", "nvfp4_device.h"]
@@ -219,6 +222,38 @@ def main():
     flop = 2.0 * M * N * K
     value = flop / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flop / (gemm_ms * 1e-3) / 1e12
+
+    # MXFP4 variant at the same shape (32-element E8M0 blocks on the scaled
+    # FP4 matrix instruction, no dequantisation): the conversion of x timed
+    # alone, then the GEMM, against the dense FP4 matrix-core peak
+    mx_w = nv.nvfp4_mxfp4_quantize(w)
+    mx_x = nv.nvfp4_mxfp4_quantize(x)
+    mx_y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(2 * args.steps)]
+    for _ in range(100):       # ~10 ms of untimed launches: the clock settles
+        nv.nvfp4_mxfp4_gemm(mx_x, mx_w, "bf16", y=mx_y)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev2[2 * i][0].record(stream)
+        nv.nvfp4_mxfp4_quantize(x, out=mx_x)
+        ev2[2 * i][1].record(stream)
+        ev2[2 * i + 1][0].record(stream)
+        nv.nvfp4_mxfp4_gemm(mx_x, mx_w, "bf16", y=mx_y)
+        ev2[2 * i + 1][1].record(stream)
+    torch.cuda.synchronize()
+    mxq_ms = sum(ev2[2 * i][0].elapsed_time(ev2[2 * i][1]) for i in range(args.steps)) / args.steps
+    mxg_ms = sum(ev2[2 * i + 1][0].elapsed_time(ev2[2 * i + 1][1])
+                 for i in range(args.steps)) / args.steps
+    mx_tflops = flop / (mxg_ms * 1e-3) / 1e12
+    mxq_bytes = M * K * 2 + M * K // 2 + M * K // 32
+    mxfp4 = {"workload": f"linear_m{M}_n{N}_k{K}, MXFP4 (E2M1, E8M0 per 32), bf16 out",
+             "gemm_us": round(mxg_ms * 1e3, 2), "tflops": round(mx_tflops, 1),
+             "peak_TFLOPs": PEAK_FP4_TFLOPS, "frac": round(mx_tflops / PEAK_FP4_TFLOPS, 4),
+             "quantize_x_us": round(mxq_ms * 1e3, 2),
+             "quantize_x_GBps": round(mxq_bytes / (mxq_ms * 1e-3) / 1e9, 1),
+             "quantize_x_frac_of_hbm": round(mxq_bytes / (mxq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del mx_w, mx_x, mx_y
 
     # skinny decode GEMMs (M = 1, 16, 32) over 16 rotating weight copies
     # (604 MB, more than the 256 MB Infinity Cache holds: cache-cold W)
@@ -481,6 +516,7 @@ def main():
         "moe_grouped": dict(moe, peak_GBps=PEAK_HBM_GBS),
         "large": large,
         "fused_quant_out": fused,
+        "mxfp4": mxfp4,
         "mid_m": dict(mid_m, workload="m{64..1024}_n8192_k8192, 16 rotating weight copies"),
         "library_reference": library,
     }

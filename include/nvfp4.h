@@ -234,6 +234,47 @@ typedef struct {
 int nvfp4_grouped_gemm_multi(int32_t count, const nvfp4_grouped_problem* problems,
                              void* stream);
 
+/*
+ * MXFP4 variant: 32-element blocks with power-of-two (E8M0) scales, the
+ * block shape the gfx950 scaled FP4 matrix instruction consumes natively,
+ * so the products need no dequantisation.  The pages define NVFP4 only
+ * (FP4 packs twice the values of FP8 and four times those of FP16: magik.net
+ * "The 3.7 PFLOPS Revelation", "Input Knowledge", item 2); this format
+ * follows the microscaling definition and shows the 4-bit format's compute
+ * ceiling on this hardware.
+ *
+ * nvfp4_mxfp4_quantize: x (fp32 | bf16) [rows, cols], row stride ld_x
+ * elements -> q [rows, cols/2] (element 2j in the low nibble of byte j) and
+ * s [rows, cols/32] E8M0 bytes (value 2^(b - 127); 255 is NaN), all DEVICE.
+ * Per 32-element block: E = floor(log2(amax)) - 2 clamped to [-127, 127]
+ * (-127 for a zero block), s = E + 127, each element the E2M1 rounding
+ * (nearest, ties to the even code, saturating at 6, sign kept) of x / 2^E;
+ * a block holding a NaN or an infinity gets s = 255 and zero nibbles.  One
+ * pass, no workspace, deterministic.
+ * Errors: NVFP4_ERR_INVALID_ARG for cols % 32 != 0, negative sizes, a bad
+ * dtype, ld_x < cols or a null pointer with rows, cols > 0;
+ * NVFP4_ERR_UNSUPPORTED for x or its rows not 16-byte aligned, q not
+ * 16-byte aligned, or a dimension above 2^30.
+ */
+int nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                         int64_t ld_x, uint8_t* q, uint8_t* s, void* stream);
+
+/*
+ * y[m, n] = sum_k A(m, k) * B(n, k) with MXFP4 operands A = (a_q [M, K/2],
+ * a_s [M, K/32]) and B = W = (b_q [N, K/2], b_s [N, K/32]), all DEVICE; no
+ * per-tensor scale.  y [M, N] (fp32 or bf16, round to nearest even), row
+ * stride ld_y.  fp32 accumulation; a NaN scale byte gives NaN outputs; terms
+ * below fp32's subnormal range are lost.  K % 128 == 0 with 16-byte aligned
+ * nibble rows and 4-byte aligned scale rows runs on the scaled FP4 matrix
+ * instruction; other shapes run a general kernel.  K == 0 writes zeros.
+ * Errors: NVFP4_ERR_INVALID_ARG for K % 32 != 0, negative sizes, a bad
+ * y_dtype, ld_y < N or a null pointer; NVFP4_ERR_UNSUPPORTED for a
+ * dimension above 2^30.
+ */
+int nvfp4_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+                     const uint8_t* b_q, const uint8_t* b_s, void* y, nvfp4_dtype y_dtype,
+                     int64_t ld_y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

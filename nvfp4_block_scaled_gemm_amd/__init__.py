@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     NVFP4_ERR_UNSUPPORTED, NVFP4_F32, NVFP4_GLOBAL_SCALE_GIVEN, NVFP4_OK, Nvfp4Error,
     Packed, load, nvfp4_gemm, nvfp4_gemm_nvfp4_out, nvfp4_gemm_nvfp4_out_raw, nvfp4_gemm_raw,
     nvfp4_grouped_gemm, nvfp4_grouped_gemm_gather_raw, nvfp4_grouped_gemm_multi,
-    nvfp4_grouped_gemm_multi_raw, nvfp4_grouped_gemm_raw,
+    nvfp4_grouped_gemm_multi_raw, nvfp4_grouped_gemm_raw, nvfp4_mxfp4_gemm,
+    nvfp4_mxfp4_gemm_raw, nvfp4_mxfp4_quantize, nvfp4_mxfp4_quantize_raw,
     nvfp4_quantize, nvfp4_quantize_noalloc_raw, nvfp4_quantize_raw, nvfp4_quantize_workspace_bytes,
 )

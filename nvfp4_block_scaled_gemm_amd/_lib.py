@@ -26,7 +26,8 @@ NVFP4_GLOBAL_SCALE_GIVEN = 1
 
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
             "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_gemm", "nvfp4_gemm_nvfp4_out", "nvfp4_grouped_gemm",
-            "nvfp4_grouped_gemm_gather", "nvfp4_grouped_gemm_multi")
+            "nvfp4_grouped_gemm_gather", "nvfp4_grouped_gemm_multi", "nvfp4_mxfp4_quantize",
+            "nvfp4_mxfp4_gemm")
 NVFP4_GROUPED_MAX_PROBLEMS = 4
 
 _lib = None
@@ -82,6 +83,10 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_grouped_gemm_gather.restype = ctypes.c_int
     lib.nvfp4_grouped_gemm_multi.argtypes = [i32, ctypes.POINTER(GroupedProblem), p]
     lib.nvfp4_grouped_gemm_multi.restype = ctypes.c_int
+    lib.nvfp4_mxfp4_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, p]
+    lib.nvfp4_mxfp4_quantize.restype = ctypes.c_int
+    lib.nvfp4_mxfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, ctypes.c_int, i64, p]
+    lib.nvfp4_mxfp4_gemm.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -418,3 +423,71 @@ def nvfp4_grouped_gemm_multi(calls, stream=None):
     st = nvfp4_grouped_gemm_multi_raw(probs, _stream(stream, devs.pop()))
     _check("nvfp4_grouped_gemm_multi", st)
     return ys
+
+
+# --------------------------------------------------------------------------
+# MXFP4 variant (32-element blocks, E8M0 scales, no per-tensor scale)
+# --------------------------------------------------------------------------
+
+def nvfp4_mxfp4_quantize_raw(x, x_dtype, rows, cols, ld_x, q, s, stream=None) -> int:
+    return load().nvfp4_mxfp4_quantize(x, x_dtype, rows, cols, ld_x, q, s, _stream(stream))
+
+
+def nvfp4_mxfp4_gemm_raw(M, N, K, a_q, a_s, b_q, b_s, y, y_dtype, ld_y, stream=None) -> int:
+    return load().nvfp4_mxfp4_gemm(M, N, K, a_q, a_s, b_q, b_s, y, y_dtype, ld_y,
+                                   _stream(stream))
+
+
+def _mx_operand(t2, what: str):
+    """(q uint8 [rows, K/2], s uint8 [rows, K/32]) on one GPU -> (rows, K, dev)."""
+    q, s = t2
+    _need(q.dim() == 2 and q.dtype == torch.uint8 and s.dtype == torch.uint8,
+          f"{what}: q and s must be 2-D uint8")
+    rows, K = q.shape[0], q.shape[1] * 2
+    _need(tuple(s.shape) == (rows, K // 32) and K % 32 == 0,
+          f"{what}: q {tuple(q.shape)} and s {tuple(s.shape)} do not pack [{rows}, {K}] in blocks of 32")
+    _need(q.is_contiguous() and s.is_contiguous(), f"{what}: q and s must be contiguous")
+    _need(q.is_cuda and s.get_device() == q.get_device(), f"{what}: q and s must be on one GPU")
+    return rows, K, q.get_device()
+
+
+def nvfp4_mxfp4_quantize(x: torch.Tensor, out=None, stream=None):
+    """x [rows, cols] fp32/bf16 on the GPU (cols % 32 == 0) -> (q uint8
+    [rows, cols/2], s uint8 [rows, cols/32]) in MXFP4; ``out`` reuses
+    buffers."""
+    _need(x.dim() == 2 and x.dtype in _DT_IN, "x: 2-D fp32 or bf16")
+    _need(x.stride(1) == 1 or x.shape[1] <= 1, "x: rows must have unit column stride")
+    _need(x.is_cuda, "x: must be on a GPU")
+    rows, cols = x.shape
+    _need(cols % 32 == 0, "x: columns must be a multiple of 32")
+    di = x.get_device()
+    with _on_stream(stream, di):
+        if out is None:
+            q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+            s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+        else:
+            q, s = out
+            r, K, dev = _mx_operand((q, s), "out")
+            _need(r == rows and K == cols and dev == di, f"out: does not pack x [{rows}, {cols}] on its GPU")
+        st = nvfp4_mxfp4_quantize_raw(_ptr(x), _DT_IN[x.dtype], rows, cols, x.stride(0), _ptr(q),
+                                      _ptr(s), _stream(None, di))
+    _check("nvfp4_mxfp4_quantize", st)
+    return q, s
+
+
+def nvfp4_mxfp4_gemm(a, b, out_dtype: str = "bf16", y: torch.Tensor | None = None, stream=None):
+    """a = (q, s) of x [M, K]; b = (q, s) of W [N, K], both MXFP4 -> y [M, N]
+    = x . W^T."""
+    M, K, da = _mx_operand(a, "a")
+    N, Kb, db = _mx_operand(b, "b")
+    _need(K == Kb and da == db, "a and b: the same K, on one GPU")
+    _need(out_dtype in _DT_OUT, f"out_dtype: one of {sorted(_DT_OUT)}")
+    code, tdt = _DT_OUT[out_dtype]
+    with _on_stream(stream, da):
+        if y is None:
+            y = torch.empty((M, N), dtype=tdt, device=a[0].device)
+        ld_y = _out(y, M, N, tdt, da)
+        st = nvfp4_mxfp4_gemm_raw(M, N, K, _ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), _ptr(y),
+                                  code, ld_y, _stream(None, da))
+    _check("nvfp4_mxfp4_gemm", st)
+    return y

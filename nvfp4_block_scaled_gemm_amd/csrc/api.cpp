@@ -260,4 +260,40 @@ int nvfp4_grouped_gemm_multi(int32_t count, const nvfp4_grouped_problem* problem
   return NVFP4_OK;
 }
 
+int nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                         int64_t ld_x, uint8_t* q, uint8_t* s, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (rows > kMaxDim || cols > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (x == nullptr || q == nullptr || s == nullptr) return NVFP4_ERR_INVALID_ARG;
+  if (ld_x < cols) return NVFP4_ERR_INVALID_ARG;
+  const int64_t esz = x_dtype == NVFP4_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ld_x * esz) % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(q, 16)) return NVFP4_ERR_UNSUPPORTED;
+  return from_hip(nvfp4::launch_mx_quantize(x, (int)x_dtype, rows, cols, ld_x, q, s,
+                                            (hipStream_t)stream));
+}
+
+int nvfp4_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+                     const uint8_t* b_q, const uint8_t* b_s, void* y, nvfp4_dtype y_dtype,
+                     int64_t ld_y, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return NVFP4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (y == nullptr || ld_y < N) return NVFP4_ERR_INVALID_ARG;
+  if (K > 0 && (a_q == nullptr || a_s == nullptr || b_q == nullptr || b_s == nullptr))
+    return NVFP4_ERR_INVALID_ARG;
+  const hipStream_t st = (hipStream_t)stream;
+  // the matrix-core kernel: whole 128-element stages, 16-byte nibble rows,
+  // 4-byte scale rows, operands (plus one tile of slack) under 4 GiB
+  if (K > 0 && K % 128 == 0 && aligned(a_q, 16) && aligned(b_q, 16) && aligned(a_s, 4) &&
+      aligned(b_s, 4) && offsets32_ok(M, K) && offsets32_ok(N, K))
+    return from_hip(nvfp4::launch_gemm_mx_mfma(M, N, K, a_q, a_s, b_q, b_s, y, (int)y_dtype, ld_y,
+                                               st));
+  return from_hip(nvfp4::launch_mx_gemm_generic(M, N, K, a_q, a_s, b_q, b_s, y, (int)y_dtype,
+                                                ld_y, st));
+}
+
 }  // extern "C"

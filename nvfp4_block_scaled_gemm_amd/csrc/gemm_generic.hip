@@ -17,13 +17,6 @@
 namespace nvfp4 {
 namespace {
 
-// 2 * E2M1 magnitude of code c = 0..7 is 0,1,2,3,4,6,8,12: one hex digit each
-// of 0xC8643210, read at digit c; bit 3 of the nibble is the sign.
-__device__ __forceinline__ int e2m1_x2(uint32_t nib) {
-  const int mag = (int)((0xC8643210u >> (4u * (nib & 7u))) & 15u);
-  return (nib & 8u) ? -mag : mag;
-}
-
 // One output y[m, n] (fp32, scaled).
 __device__ __forceinline__ float dot(int64_t M, int64_t N, int64_t K,
                                      const uint8_t* __restrict__ a_q,

@@ -588,6 +588,282 @@ hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOp
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 GEMM on the scaled FP4 matrix instruction.
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in E2M1 multiplies a
+// 32 x 64 by a 64 x 32 fragment of packed nibbles and applies one E8M0
+// scale per lane: lane L holds row (or column) L % 32 and 32 consecutive
+// K-elements, exactly one 32-element block, plus that block's scale byte
+// (checked against an exact product on every lane).  No dequantisation is
+// left to the vector unit, so the kernel is the same LDS ring as above with
+// the products issued straight from the fragment reads:
+//  * a stage is 128 K-elements: 64 bytes of nibbles and 4 scale bytes per
+//    row, moved HBM -> LDS by direct loads into a 4-deep ring, rows XOR-
+//    swizzled in 16-byte chunks as above;
+//  * K is permuted inside a stage (identically for both operands): lane
+//    half g owns blocks 2g and 2g + 1 of the stage, so MFMA step t (0, 1)
+//    reads 16-byte chunk 2g + t of its row and scale byte t of the two it
+//    loads at once;
+//  * per stage: step 0's products run while the step-1 fragments are read
+//    and the ring is refilled; the workgroup then syncs on stage s + 1, and
+//    step 1's products run while stage s + 1's step-0 fragments are read.
+//    Every stage issues the same loads (past the last stage a harmless
+//    reload of it into a slot no stage reads again), so the waits are fixed.
+constexpr int kMxScBytes = 4;   // E8M0 bytes per row per stage (128 / 32)
+
+template <int BM, int BN>
+struct SmemMx {
+  static constexpr int kANib = 0;
+  static constexpr int kBNib = kANib + BM * kRowBytes;
+  static constexpr int kASc = kBNib + BN * kRowBytes;
+  static constexpr int kBSc = kASc + BM * kMxScBytes;
+  static constexpr int kBytes = kBSc + BN * kMxScBytes;  // one stage
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct CfgMx {
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int kANibLoads = BM * kRowBytes / 1024 / kWaves;
+  static constexpr int kBNibLoads = BN * kRowBytes / 1024 / kWaves;
+  // scale loads (4 bytes per lane, 256 bytes per instruction); with fewer
+  // than one per wave the extra waves repeat one exactly (same bytes to the
+  // same LDS slot), so every wave issues the same number of loads
+  static constexpr int kAScTotal = (BM * kMxScBytes + 255) / 256;
+  static constexpr int kBScTotal = (BN * kMxScBytes + 255) / 256;
+  static constexpr int kAScLoads = kAScTotal >= kWaves ? kAScTotal / kWaves : 1;
+  static constexpr int kBScLoads = kBScTotal >= kWaves ? kBScTotal / kWaves : 1;
+  static constexpr int kLoads = kANibLoads + kBNibLoads + kAScLoads + kBScLoads;
+  static_assert(kANibLoads >= 1 && kBNibLoads >= 1, "tile too small for the load split");
+  static_assert(BM * kMxScBytes % 256 == 0 && BN * kMxScBytes % 256 == 0,
+                "whole scale-load instructions");
+  static_assert((kAScTotal < kWaves || kAScTotal % kWaves == 0) &&
+                    (kBScTotal < kWaves || kBScTotal % kWaves == 0),
+                "scale loads split evenly over the waves");
+  static __device__ __forceinline__ int asc_slot(int w) {
+    return kAScTotal >= kWaves ? w * kAScLoads : w % kAScTotal;
+  }
+  static __device__ __forceinline__ int bsc_slot(int w) {
+    return kBScTotal >= kWaves ? w * kBScLoads : w % kBScTotal;
+  }
+};
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 16-byte fragment chunk of step t for lane half g (rows XOR-swizzled).
+__device__ __forceinline__ u32x4 read_mx_chunk(const uint8_t* nib, int row, int g, int t) {
+  return *reinterpret_cast<const u32x4*>(nib + row * kRowBytes + (((2 * g + t) ^ swz(row)) << 4));
+}
+
+// Scale bytes of blocks 2g, 2g + 1 of the lane's row: byte t is step t's.
+__device__ __forceinline__ uint32_t read_mx_scales(const uint8_t* sc, int row, int g) {
+  return *reinterpret_cast<const uint16_t*>(sc + row * kMxScBytes + 2 * g);
+}
+
+template <int T>
+__device__ __forceinline__ f32x16 mx_mfma(const u32x4& a, uint32_t sa, const u32x4& b,
+                                          uint32_t sb, const f32x16& c) {
+  // E2M1 operands (format code 4) occupy the first four registers
+  const i32x8 a8 = __builtin_shufflevector(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, a),
+                                           0, 1, 2, 3, 0, 1, 2, 3);
+  const i32x8 b8 = __builtin_shufflevector(__builtin_bit_cast(i32x4, b), __builtin_bit_cast(i32x4, b),
+                                           0, 1, 2, 3, 0, 1, 2, 3);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, T, (int)sa, T, (int)sb);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mx_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
+    const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s, void* __restrict__ y,
+    int y_dtype, int64_t ld_y, uint32_t y_bytes, int y_flags) {
+  static_assert(kStages == 4, "the ring is 4 deep");
+  using C = CfgMx<BM, BN, WAVES_M, WAVES_N>;
+  using L = SmemMx<BM, BN>;
+  constexpr int FM = C::FM, FN = C::FN, NF = FM + FN;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int li = lane & 31, lg = lane >> 5;
+
+  int tm, tn;
+  tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t rowq = (uint32_t)(K / 2), rows = (uint32_t)(K / 32);
+  const int nstage = K / kBK;
+
+  // per-lane source offsets (rows past M / N clamped to the last row: they
+  // only feed outputs that are not stored)
+  uint32_t a_nib_off[C::kANibLoads], b_nib_off[C::kBNibLoads];
+  uint32_t a_sc_off[C::kAScLoads], b_sc_off[C::kBScLoads];
+#pragma unroll
+  for (int i = 0; i < C::kANibLoads; ++i) {
+    const int slot = (wave * C::kANibLoads + i) * 64 + lane;
+    const int r = slot >> 2, phys = slot & 3;
+    a_nib_off[i] = (uint32_t)min(m0 + r, M - 1) * rowq + ((phys ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kBNibLoads; ++i) {
+    const int slot = (wave * C::kBNibLoads + i) * 64 + lane;
+    const int r = slot >> 2, phys = slot & 3;
+    b_nib_off[i] = (uint32_t)min(n0 + r, N - 1) * rowq + ((phys ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kAScLoads; ++i) {
+    const int slot = (C::asc_slot(wave) + i) * 64 + lane;  // 4-byte slot = one row
+    a_sc_off[i] = (uint32_t)min(m0 + slot, M - 1) * rows;
+  }
+#pragma unroll
+  for (int i = 0; i < C::kBScLoads; ++i) {
+    const int slot = (C::bsc_slot(wave) + i) * 64 + lane;
+    b_sc_off[i] = (uint32_t)min(n0 + slot, N - 1) * rows;
+  }
+  const uint32_t aq_bytes = (uint32_t)M * rowq, bq_bytes = (uint32_t)N * rowq;
+  const uint32_t as_bytes = (uint32_t)M * rows, bs_bytes = (uint32_t)N * rows;
+
+  // the loads of stage st into ring slot `slot` (st past the end reloads
+  // the last stage)
+  auto issue = [&](int st, int slot) {
+    const int src = min(st, nstage - 1);
+    uint8_t* base = smem + slot * L::kBytes;
+#pragma unroll
+    for (int i = 0; i < C::kANibLoads; ++i)
+      buffer_load_lds16(a_q, aq_bytes, base + L::kANib + (wave * C::kANibLoads + i) * 1024,
+                        a_nib_off[i], (uint32_t)src * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < C::kBNibLoads; ++i)
+      buffer_load_lds16(b_q, bq_bytes, base + L::kBNib + (wave * C::kBNibLoads + i) * 1024,
+                        b_nib_off[i], (uint32_t)src * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < C::kAScLoads; ++i)
+      buffer_load_lds4(a_s, as_bytes, base + L::kASc + (C::asc_slot(wave) + i) * 256,
+                       a_sc_off[i], (uint32_t)src * kMxScBytes);
+#pragma unroll
+    for (int i = 0; i < C::kBScLoads; ++i)
+      buffer_load_lds4(b_s, bs_bytes, base + L::kBSc + (C::bsc_slot(wave) + i) * 256,
+                       b_sc_off[i], (uint32_t)src * kMxScBytes);
+  };
+
+  auto frag_row = [&](int f) { return f < FM ? wm * C::TM + f * 32 + li : wn * C::TN + (f - FM) * 32 + li; };
+  auto nib_base = [&](int st, int f) {
+    return smem + (st & (kStages - 1)) * L::kBytes + (f < FM ? L::kANib : L::kBNib);
+  };
+  auto sc_base = [&](int st, int f) {
+    return smem + (st & (kStages - 1)) * L::kBytes + (f < FM ? L::kASc : L::kBSc);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  u32x4 f0[NF], f1[NF];  // step 0 / step 1 fragments of the current stage
+  uint32_t sc[NF];       // their scale pairs
+
+  // prologue: stages 0..2 in flight, stage 0's step-0 fragments read
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st) issue(st, st);
+  wait_vmcnt<2 * C::kLoads>();
+  workgroup_barrier();
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    f0[f] = read_mx_chunk(nib_base(0, f), frag_row(f), lg, 0);
+    sc[f] = read_mx_scales(sc_base(0, f), frag_row(f), lg);
+  }
+
+  constexpr int Q = FM * FN;                  // products per step
+  constexpr int kIssueAt = NF < Q - 1 ? NF : Q - 1;  // product after which the refill goes
+  for (int s = 0; s < nstage; ++s) {
+    wait_lgkmcnt0();  // stage s's step-0 fragments
+    // step 0: products of f0 while f1 is read and the ring is refilled
+    static_for<Q>([&](auto ic) {
+      constexpr int I = decltype(ic)::value, i = I / FN, j = I % FN;
+      acc[i][j] = mx_mfma<0>(f0[i], sc[i], f0[FM + j], sc[FM + j], acc[i][j]);
+      if constexpr (I < NF) f1[I] = read_mx_chunk(nib_base(s, I), frag_row(I), lg, 1);
+      if constexpr (I == kIssueAt) issue(s + kStages - 1, (s + kStages - 1) & (kStages - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<(NF > Q ? NF - Q : 0)>([&](auto ic) {
+      constexpr int I = Q + decltype(ic)::value;
+      f1[I] = read_mx_chunk(nib_base(s, I), frag_row(I), lg, 1);
+    });
+    // the step-1 fragments are in registers and this wave's loads of stage
+    // s + 1 have landed; after the barrier every wave's have, and every
+    // wave is done reading stage s - 1 (whose slot the refill above took)
+    wait_lgkmcnt0();
+    wait_vmcnt<2 * C::kLoads>();
+    workgroup_barrier();
+    // step 1: products of f1 while stage s + 1's step-0 fragments are read
+    const bool next = s + 1 < nstage;
+    uint32_t nsc[NF];
+    static_for<Q>([&](auto ic) {
+      constexpr int I = decltype(ic)::value, i = I / FN, j = I % FN;
+      acc[i][j] = mx_mfma<1>(f1[i], sc[i], f1[FM + j], sc[FM + j], acc[i][j]);
+      if constexpr (I < NF) {
+        if (next) {
+          f0[I] = read_mx_chunk(nib_base(s + 1, I), frag_row(I), lg, 0);
+          nsc[I] = read_mx_scales(sc_base(s + 1, I), frag_row(I), lg);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<(NF > Q ? NF - Q : 0)>([&](auto ic) {
+      constexpr int I = Q + decltype(ic)::value;
+      if (next) {
+        f0[I] = read_mx_chunk(nib_base(s + 1, I), frag_row(I), lg, 0);
+        nsc[I] = read_mx_scales(sc_base(s + 1, I), frag_row(I), lg);
+      }
+    });
+    if (next) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) sc[f] = nsc[f];
+    }
+  }
+
+  // epilogue: the ring's last (padding) loads land, then each wave stages
+  // its tile in its own region of the idle ring
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  const bool whole = y_bytes != 0 && m0 + BM <= M && n0 + BN <= N;
+  const bool vec = (y_flags & 1) != 0;
+  const int row0 = m0 + wm * C::TM, col0 = n0 + wn * C::TN;
+  constexpr int kRegion = C::TM * (C::TN * 2 + 16);
+  static_assert(C::kWaves * kRegion <= kStages * L::kBytes, "epilogue staging exceeds the ring");
+  workgroup_barrier();
+  uint8_t* region = smem + wave * kRegion;
+  if (y_dtype == 0)
+    store_tile<0>(acc, 1.0f, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
+  else
+    store_tile<1>(acc, 1.0f, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+hipError_t launch_mx_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+                         const uint8_t* b_q, const uint8_t* b_s, void* y, int y_dtype,
+                         int64_t ld_y, hipStream_t stream) {
+  using L = SmemMx<BM, BN>;
+  using C = CfgMx<BM, BN, WAVES_M, WAVES_N>;
+  const int smem = kStages * L::kBytes;
+  auto kern = gemm_mx_kernel<BM, BN, WAVES_M, WAVES_N>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t extent = ((M - 1) * ld_y + N) * (y_dtype == 0 ? 4 : 2);
+  const uint32_t y_bytes = extent < (int64_t)0xFFFFFFFF ? (uint32_t)extent : 0u;
+  const int y_flags = ((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ld_y % 8 == 0) ? 1 : 0;
+  kern<<<(unsigned)tiles, C::kThreads, smem, stream>>>((int)M, (int)N, (int)K, a_q, a_s, b_q, b_s,
+                                                        y, y_dtype, ld_y, y_bytes, y_flags);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperand b,
@@ -608,6 +884,20 @@ hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a, Pa
   if (tiles(128, 64) == 256 || tiles(64, 64) > 256)
     return launch_cfg<128, 64, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
   return launch_cfg<64, 64, 2, 2>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
+}
+
+hipError_t launch_gemm_mx_mfma(int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
+                               const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                               void* y, int y_dtype, int64_t ld_y, hipStream_t stream) {
+  // the same tile ladder as the NVFP4 kernel
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (M >= 256 && N >= 256 && tiles(256, 256) >= 256)
+    return launch_mx_cfg<256, 256, 2, 2>(M, N, K, a_q, a_s, b_q, b_s, y, y_dtype, ld_y, stream);
+  if (M >= 256 && N >= 128 && tiles(256, 128) >= 256)
+    return launch_mx_cfg<256, 128, 2, 2>(M, N, K, a_q, a_s, b_q, b_s, y, y_dtype, ld_y, stream);
+  if (tiles(128, 128) >= 256 || tiles(128, 64) > 256)
+    return launch_mx_cfg<128, 128, 2, 2>(M, N, K, a_q, a_s, b_q, b_s, y, y_dtype, ld_y, stream);
+  return launch_mx_cfg<64, 64, 2, 2>(M, N, K, a_q, a_s, b_q, b_s, y, y_dtype, ld_y, stream);
 }
 
 }  // namespace nvfp4

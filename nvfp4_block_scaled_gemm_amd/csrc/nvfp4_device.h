@@ -80,6 +80,13 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// 2 * E2M1 magnitude of code c = 0..7 is 0,1,2,3,4,6,8,12: one hex digit each
+// of 0xC8643210, read at digit c; bit 3 of the nibble is the sign.
+__device__ __forceinline__ int e2m1_x2(uint32_t nib) {
+  const int mag = (int)((0xC8643210u >> (4u * (nib & 7u))) & 15u);
+  return (nib & 8u) ? -mag : mag;
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);

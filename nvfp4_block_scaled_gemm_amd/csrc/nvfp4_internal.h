@@ -48,6 +48,19 @@ hipError_t launch_gemm_grouped_generic(int32_t G, const int32_t* m_offsets,
                                        int64_t N, int64_t K, PackedOperand a, PackedOperand b,
                                        void* y, int y_dtype, int64_t ld_y, hipStream_t stream);
 
+// mxfp4.hip: MXFP4 conversion (cols % 32 == 0, 16-byte aligned x rows and
+// q) and the general MXFP4 GEMM (any M, N, K % 32 == 0).
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t* q, uint8_t* s, hipStream_t stream);
+hipError_t launch_mx_gemm_generic(int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
+                                  const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                                  void* y, int y_dtype, int64_t ld_y, hipStream_t stream);
+// gemm_mfma.hip: MXFP4 on the scaled FP4 matrix instruction; K % 128 == 0,
+// 16-byte aligned nibble rows, 4-byte aligned scale rows.
+hipError_t launch_gemm_mx_mfma(int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
+                               const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                               void* y, int y_dtype, int64_t ld_y, hipStream_t stream);
+
 // gemm_mfma.hip: K % 128 == 0, 16-byte aligned operand rows.
 hipError_t launch_gemm_mfma(int64_t M, int64_t N, int64_t K, PackedOperand a,
                             PackedOperand b, void* y, int y_dtype, int64_t ld_y,

@@ -332,3 +332,60 @@ def test_grouped_multi_argument_checks(probs, count, status):
 def test_grouped_multi_null_problem_list():
     assert nv.load().nvfp4_grouped_gemm_multi(1, None, None) == nv.NVFP4_ERR_INVALID_ARG
     assert nv.load().nvfp4_grouped_gemm_multi(0, None, None) == nv.NVFP4_OK
+
+
+def _mxq(**kw):
+    args = dict(x=P16, x_dtype=nv.NVFP4_BF16, rows=4, cols=64, ld_x=64, q=P16, s=P16)
+    args.update(kw)
+    return nv.load().nvfp4_mxfp4_quantize(args["x"], args["x_dtype"], args["rows"], args["cols"],
+                                          args["ld_x"], args["q"], args["s"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cols=48), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(rows=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x_dtype=5), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(s=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(ld_x=32), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(x=P8), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(q=P8), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(ld_x=68), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(rows=1 << 31), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(rows=0), nv.NVFP4_OK),
+    (dict(cols=0, ld_x=0), nv.NVFP4_OK),
+])
+def test_mxfp4_quantize_argument_checks(kw, status):
+    assert _mxq(**kw) == status
+
+
+def _mxg(**kw):
+    args = dict(M=4, N=8, K=128, a_q=P16, a_s=P16, b_q=P16, b_s=P16, y=P16,
+                y_dtype=nv.NVFP4_BF16, ld_y=8)
+    args.update(kw)
+    order = ("M", "N", "K", "a_q", "a_s", "b_q", "b_s", "y", "y_dtype", "ld_y")
+    return nv.load().nvfp4_mxfp4_gemm(*[args[k] for k in order], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=48), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(M=-1), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y_dtype=2), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(ld_y=4), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(y=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(b_s=NULL), nv.NVFP4_ERR_INVALID_ARG),
+    (dict(N=1 << 31, ld_y=1 << 31), nv.NVFP4_ERR_UNSUPPORTED),
+    (dict(M=0), nv.NVFP4_OK),
+    (dict(N=0, ld_y=0), nv.NVFP4_OK),
+])
+def test_mxfp4_gemm_argument_checks(kw, status):
+    assert _mxg(**kw) == status
+
+
+def test_mxfp4_binding_rejects_mismatched_tensors():
+    q = torch.zeros((4, 32), dtype=torch.uint8)
+    s = torch.zeros((4, 4), dtype=torch.uint8)   # K = 64 needs 2 scale bytes per row
+    with pytest.raises(ValueError):
+        nv.nvfp4_mxfp4_gemm((q, s), (q, s))
+    with pytest.raises(ValueError):
+        nv.nvfp4_mxfp4_quantize(torch.zeros((4, 48), dtype=torch.bfloat16))
