@@ -16,8 +16,8 @@
 //    workgroup reads them).
 //  * Every chunk goes to LDS with 16-byte buffer-to-LDS loads, 1 KB per
 //    instruction, each covering whole 128-byte lines of two rows.  The ring
-//    holds 4 chunks, 3 of them in flight while one is multiplied (deeper
-//    rings measured slower).
+//    holds 3 chunks, 2 of them in flight while one is multiplied (for 5-32
+//    tokens; 2 or 4 slots measured slower, deeper rings slower still).
 //    One barrier per chunk separates the landing of chunk c from the reuse
 //    of the slot that held chunk c - 1.
 //  * Inside a chunk wave w takes K elements [128w, 128w + 128): lane (li, lq)
@@ -304,12 +304,14 @@ hipError_t launch(int64_t M, int64_t N, int64_t K, PackedOperand a, PackedOperan
 hipError_t launch_gemm_decode_lds(int64_t M, int64_t N, int64_t K, PackedOperand a,
                                   PackedOperand b, void* y, int y_dtype, int64_t ld_y,
                                   hipStream_t stream, QuantOut qo) {
-  // Four ring slots (three chunks in flight) stream faster than deeper rings
-  // on the MI355X: M = 1 / 16 in ~10.8 / ~11.6 us at N = K = 8192 against
-  // ~12.7 / ~12.4 us with 7 / 5 slots.
+  // Ring depth, measured on the MI355X at N = K = 8192 (cache-cold W, back
+  // to back): 3 slots take M = 16 / 32 in ~10.9 / ~13.4 us against ~11.6 /
+  // ~14.1 us with 4 slots and ~11.8 / ~13.6 us with 2; 5 or more slots (M =
+  // 1 / 16 in ~12.7 / ~12.4 us with 7 / 5) are slower still.  Up to 4
+  // tokens (K != 8192: the whole-row kernel takes K = 8192) keep 4 slots.
   if (M <= 4) return launch<1, 4, 4>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
-  if (M <= 16) return launch<1, 16, 4>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
-  return launch<2, 32, 4>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
+  if (M <= 16) return launch<1, 16, 3>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
+  return launch<2, 32, 3>(M, N, K, a, b, y, y_dtype, ld_y, stream, qo);
 }
 
 }  // namespace nvfp4

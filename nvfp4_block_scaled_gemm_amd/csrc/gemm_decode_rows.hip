@@ -125,6 +125,7 @@ __global__ __launch_bounds__(64 * W, 1) void decode_rows_kernel(
   const int nchunks = g < groups ? (groups - g + G - 1) / G : 0;  // uniform
   constexpr uint32_t qrow = K / 2, srow = K / 16;
   const uint32_t wq_bytes = (uint32_t)N * qrow, ws_bytes = (uint32_t)N * srow;
+  const float alpha = a_g[0] * b_g[0];  // read early: off the end of the kernel
 
   // ---- the tokens' operand: B column li = (part li / R, token slot
   // li % R) of token group nb; lane (li, lq) holds the 8 S elements starting
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(64 * W, 1) void decode_rows_kernel(
   // Every wave issues exactly kPerWave loads per chunk (chunks past the end
   // and padding read nothing), so one fixed vmcnt wait per chunk suffices.
   auto issue = [&](int c, int slot) {
-    const bool live = c < nchunks;
+    const bool live = G * c + g < groups;  // c < nchunks, without the division
     const uint32_t row0 = (uint32_t)(R * (G * c + g));
 #pragma unroll
     for (int k = 0; k < C::kPerWave; ++k) {
@@ -269,7 +270,6 @@ __global__ __launch_bounds__(64 * W, 1) void decode_rows_kernel(
   __syncthreads();
   // every chunk's outputs: token t, row r of chunk c, over waves and parts
   // in fixed order; consecutive threads write consecutive output columns
-  const float alpha = a_g[0] * b_g[0];
   for (int idx = tid; idx < nchunks * M * R; idx += kThreads) {
     const int c = idx / (M * R), t = (idx / R) % M, r = idx % R;
     const int nb = t / R, tt = t % R;
@@ -331,12 +331,13 @@ hipError_t launch_gemm_decode_rows(int64_t M, int64_t N, int64_t K, PackedOperan
                                    hipStream_t stream) {
   if (!decode_rows_shape(M, K) || (y_dtype != 0 && y_dtype != 1)) return hipErrorInvalidValue;
   // Measured on the MI355X at N = K = 8192 (cache-cold W, back to back):
-  // 4-row chunks with a 4-slot ring take M = 1 in ~9.9 us against ~10.8 us
-  // for the LDS-tile kernel.  From 5 tokens on the products cost more than
-  // the tile kernel's (8-row chunks keep only half of each MFMA, 16-row
-  // chunks fit only a 2-slot ring), so those shapes go there.
+  // 4-row chunks with a 3-slot ring take M = 1 in ~9.3 us (a 4-slot ring:
+  // ~9.9 us) against ~10.8 us for the LDS-tile kernel.  From 5 tokens on
+  // the products cost more than the tile kernel's (8-row chunks keep only
+  // half of each MFMA, 16-row chunks fit only a 2-slot ring), so those
+  // shapes go there.
   hipError_t err = hipSuccess;
-  const bool done = launch<4, 8, 1, 4, 8>(M, N, a, b, y, y_dtype, ld_y, stream, &err);
+  const bool done = launch<4, 8, 1, 3, 8>(M, N, a, b, y, y_dtype, ld_y, stream, &err);
   // very wide outputs: the LDS-ring tile kernel (same operand requirements)
   if (!done) return launch_gemm_decode_lds(M, N, K, a, b, y, y_dtype, ld_y, stream);
   return err;
