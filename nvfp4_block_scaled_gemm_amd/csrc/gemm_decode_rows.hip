@@ -38,8 +38,8 @@
 //    dependent MFMA chain), and its partial sums are only parked: each wave
 //    stores the lanes that hold kept products (1 / P of them) to a compact
 //    per-chunk area in LDS.  After the last chunk all threads sum every
-//    chunk's partials (fixed order: waves, then parts), scale by
-//    fl32(ga gb) and store fp32 or bf16.
+//    chunk's partials (a fixed pairwise order over waves and parts), scale
+//    by fl32(ga gb) and store fp32 or bf16.
 #include "nvfp4_device.h"
 #include "nvfp4_dispatch.h"
 #include "nvfp4_internal.h"
@@ -126,6 +126,7 @@ __global__ __launch_bounds__(64 * W, 1) void decode_rows_kernel(
   constexpr uint32_t qrow = K / 2, srow = K / 16;
   const uint32_t wq_bytes = (uint32_t)N * qrow, ws_bytes = (uint32_t)N * srow;
   const float alpha = a_g[0] * b_g[0];  // read early: off the end of the kernel
+  const uint32_t inv_m = (65535u + (uint32_t)M) / (uint32_t)M;  // ceil(65536 / M)
 
   // ---- the tokens' operand: B column li = (part li / R, token slot
   // li % R) of token group nb; lane (li, lq) holds the 8 S elements starting
@@ -268,21 +269,31 @@ __global__ __launch_bounds__(64 * W, 1) void decode_rows_kernel(
   }
   wait_vmcnt<0>();
   __syncthreads();
-  // every chunk's outputs: token t, row r of chunk c, over waves and parts
-  // in fixed order; consecutive threads write consecutive output columns
+  // every chunk's outputs: token t, row r of chunk c, summed over waves and
+  // parts in a fixed pairwise order; consecutive threads write consecutive
+  // output columns.  All W P partials of an output are read before the
+  // first add, so the reads overlap instead of waiting one by one.
   for (int idx = tid; idx < nchunks * M * R; idx += kThreads) {
-    const int c = idx / (M * R), t = (idx / R) % M, r = idx % R;
+    // idx = (c M + t) R + r; c by a multiply and a shift, exact while
+    // c M + t < 65536 / M (the LDS holds far fewer chunks' partials)
+    const int ct = idx / R, r = idx % R;
+    const int c = (int)(((uint32_t)ct * inv_m) >> 16), t = ct - c * M;
     const int nb = t / R, tt = t % R;
-    float s = 0.0f;
+    static_assert((kWaves * P & (kWaves * P - 1)) == 0, "pairwise sum over a power of two");
+    float v[kWaves * P];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int k = (R * p + tt) * (R / 4) + (r >> 2);
-        s += part[(((c * NB + nb) * kWaves + w) * (4 * R) + k) * 4 + (r & 3)];
+        v[w * P + p] = part[(((c * NB + nb) * kWaves + w) * (4 * R) + k) * 4 + (r & 3)];
       }
+#pragma unroll
+    for (int h = kWaves * P / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int i = 0; i < h; ++i) v[i] += v[i + h];
     const int n = R * (G * c + g) + r;
-    if (n < N) store_out(y, (int64_t)t * ld_y + n, s * alpha, y_dtype);
+    if (n < N) store_out(y, (int64_t)t * ld_y + n, v[0] * alpha, y_dtype);
   }
 }
 
