@@ -28,13 +28,14 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-# The decode kernels run for ~10 us, so the latency of their first kernel-
-# argument loads shows in the total: there the compiler is asked to have the
-# leading 14 argument dwords preloaded into SGPRs at wave launch (gfx950; the
-# code object keeps a fallback entry that loads them when the firmware does
-# not preload).
+# The decode-sized kernels (decode GEMMs, the quantiser's passes at a few
+# rows, the 33-96 row GEMM) run for a few to ~20 us, so the latency of their
+# first kernel-argument loads shows in the total: for them the compiler is
+# asked to have the leading 14 argument dwords preloaded into SGPRs at wave
+# launch (gfx950; the code object keeps a fallback entry that loads them when
+# the firmware does not preload).
 PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=14"]
-EXTRA_FLAGS = {"gemm_decode_rows.hip": PRELOAD, "gemm_decode_lds.hip": PRELOAD}
+EXTRA_FLAGS = {f: PRELOAD for f in ("gemm_decode_rows.hip", "gemm_decode_lds.hip", "gemm_skinny.hip", "quantize.hip")}
 
 
 def hipcc() -> str:
