@@ -547,19 +547,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mfma_kernel(
   static_assert(C::kWaves * kRegion <= kStages * L::kBytes, "epilogue staging exceeds the ring");
   workgroup_barrier();
   uint8_t* region = smem + wave * kRegion;
+  // the lane index again, from the hardware lane counter: an expression the
+  // compiler cannot equate with the one before the main loop, so nothing
+  // lane-dependent has to stay live (or spill) across the loop for this
+  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   if (y_dtype == 2) {
     static_assert((C::FM >= 2 ? C::FM / 2 : 1) * 32 * (C::TN * 4 + 16) <= kRegion,
                   "quantising epilogue staging exceeds the wave's region");
     const float g = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(qo.g[0])));
     const enc::EncodeParams P = enc::make_params(g);
     const int mode = enc::encode_mode(g);
-    if (mode == 1) quant_tile<1>(acc, alpha, M, N, row0, col0, lane, region, qo, P);
-    else if (mode == 0) quant_tile<0>(acc, alpha, M, N, row0, col0, lane, region, qo, P);
-    else quant_tile<2>(acc, alpha, M, N, row0, col0, lane, region, qo, P);
+    if (mode == 1) quant_tile<1>(acc, alpha, M, N, row0, col0, elane, region, qo, P);
+    else if (mode == 0) quant_tile<0>(acc, alpha, M, N, row0, col0, elane, region, qo, P);
+    else quant_tile<2>(acc, alpha, M, N, row0, col0, elane, region, qo, P);
   } else if (y_dtype == 0) {
-    store_tile<0>(acc, alpha, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
+    store_tile<0>(acc, alpha, y, ld_y, M, N, row0, col0, elane, whole, vec, y_bytes, region);
   } else {
-    store_tile<1>(acc, alpha, y, ld_y, M, N, row0, col0, lane, whole, vec, y_bytes, region);
+    store_tile<1>(acc, alpha, y, ld_y, M, N, row0, col0, elane, whole, vec, y_bytes, region);
   }
 }
 
