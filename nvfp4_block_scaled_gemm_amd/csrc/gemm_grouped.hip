@@ -35,7 +35,9 @@
 //    v_mfma_f32_16x16x32_f16: four 16-row weight fragments x one or two
 //    16-token fragments, 16 steps per job (K is permuted identically on both
 //    sides).  Each token fragment is dequantised once per step and reused by
-//    the four weight fragments.
+//    the four weight fragments.  The steps are software-pipelined: step T's
+//    MFMAs go out beside step T+1's dequantisation, so with one wave per
+//    SIMD the matrix core and the vector unit still overlap.
 //  * After the last slice of an item-chunk the wave scales by ga * gb[e] and
 //    stores its 64 x ntok outputs, four consecutive columns per store.
 //  * One launch can carry several independent grouped GEMMs (up to
@@ -406,8 +408,46 @@ __device__ __forceinline__ void run_problem(int pi, const int* pp, int units, in
     }
     const Scales sx0[2] = {to_scales(xs[S].s[0][0]), to_scales(xs[S].s[0][1])};
     const int ntok = c.r1 - c.c0;
-    // step T (0..15) uses dword T of the lane's 64 bytes: block T/2, i.e.
-    // scale pair word T/8, block (T/2) % 4 within it
+    // Step T (0..15) uses dword T of the lane's 64 bytes: block T/2, i.e.
+    // scale pair word T/8, block (T/2) % 4 within it.  Software-pipelined:
+    // the MFMAs of step T go out beside the dequantisation of step T+1, so
+    // the matrix core and the vector unit overlap inside the one wave a
+    // SIMD runs.
+    auto run_steps = [&](auto ntc) {
+      constexpr int NT = decltype(ntc)::value;  // token fragments (1 or 2)
+      Scales sx1[2];
+      if constexpr (NT == 2) {
+        sx1[0] = to_scales(xs[S].s[1][0]);
+        sx1[1] = to_scales(xs[S].s[1][1]);
+      }
+      auto dq = [&](auto tc, f16x8(&a)[kFrags], f16x8(&b)[2]) {
+        constexpr int T = decltype(tc)::value, Q = T / 4, D = T % 4, H = T / 8, TT = T % 8;
+        b[0] = dequant_step<TT>(xs[S].q[0][Q][D], sx0[H]);
+        if constexpr (NT == 2) b[1] = dequant_step<TT>(xs[S].q[1][Q][D], sx1[H]);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) a[f] = dequant_step<TT>(w[f][Q][D], sw[f][H]);
+      };
+      f16x8 a[kFrags], b[2];
+      dq(std::integral_constant<int, 0>{}, a, b);
+      static_for<16>([&](auto tc) {
+        constexpr int T = decltype(tc)::value;
+        f16x8 an[kFrags], bn[2];
+        if constexpr (T + 1 < 16) dq(std::integral_constant<int, T + 1>{}, an, bn);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) {
+          acc[f][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], b[0], acc[f][0], 0, 0, 0);
+          if constexpr (NT == 2)
+            acc[f][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], b[1], acc[f][1], 0, 0, 0);
+        }
+        if constexpr (T + 1 < 16) {
+#pragma unroll
+          for (int f = 0; f < kFrags; ++f) a[f] = an[f];
+          b[0] = bn[0];
+          b[1] = bn[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
     if (ntok > 16) {  // wave-uniform
       // fresh copies of the shared operands, so the compiler cannot hoist
       // the two branches' common dequantisation above the branch (that
@@ -418,30 +458,9 @@ __device__ __forceinline__ void run_problem(int pi, const int* pp, int units, in
         for (int f = 0; f < kFrags; ++f) opaque(w[f][i]);
         opaque(xs[S].q[0][i]);
       }
-      const Scales sx1[2] = {to_scales(xs[S].s[1][0]), to_scales(xs[S].s[1][1])};
-      static_for<16>([&](auto tc) {
-        constexpr int T = decltype(tc)::value, Q = T / 4, D = T % 4, H = T / 8, TT = T % 8;
-        const f16x8 b0 = dequant_step<TT>(xs[S].q[0][Q][D], sx0[H]);
-        const f16x8 b1 = dequant_step<TT>(xs[S].q[1][Q][D], sx1[H]);
-#pragma unroll
-        for (int f = 0; f < kFrags; ++f) {
-          const f16x8 a = dequant_step<TT>(w[f][Q][D], sw[f][H]);
-          acc[f][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, acc[f][0], 0, 0, 0);
-          acc[f][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b1, acc[f][1], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep each step's dequant beside its MFMAs
-      });
+      run_steps(std::integral_constant<int, 2>{});
     } else {
-      static_for<16>([&](auto tc) {
-        constexpr int T = decltype(tc)::value, Q = T / 4, D = T % 4, H = T / 8, TT = T % 8;
-        const f16x8 b0 = dequant_step<TT>(xs[S].q[0][Q][D], sx0[H]);
-#pragma unroll
-        for (int f = 0; f < kFrags; ++f) {
-          const f16x8 a = dequant_step<TT>(w[f][Q][D], sw[f][H]);
-          acc[f][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, acc[f][0], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      run_steps(std::integral_constant<int, 1>{});
     }
     if (c.k == P.nunits - 1) {
       // acc[f][g] reg r: weight row n0 + 16f + 4*lq + r, token c0 + 16g + li
