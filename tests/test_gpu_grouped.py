@@ -47,6 +47,9 @@ def _run(counts, N, K, out, seed):
     ([33, 64, 2, 0, 31, 32, 130], 200, 1536),
     ([33, 0, 2, 31, 16], 72, 768),
     ([5, 9], 30, 48),
+    # experts of 31 to 200 rows: chunk runs ending in 1 to 32 tokens, on a
+    # ragged last weight tile
+    ([63, 64, 65, 0, 96, 97, 31, 128, 129, 200, 1], 136, 1024),
 ])
 def test_ragged_groups(counts, N, K):
     for out in ("f32", "bf16"):
@@ -100,6 +103,7 @@ def test_exhaustive_dequant_identity(counts):
     ([33, 64, 2, 0, 31], 130, 1024, 20),
     ([7, 9], 40, 768, 12),
     ([5, 9], 30, 48, 6),
+    ([63, 64, 65, 97, 129, 200], 136, 1024, 300),
 ])
 def test_gather_rows(counts, N, K, a_rows):
     """Grouped rows read through an index list (duplicates, and two indices

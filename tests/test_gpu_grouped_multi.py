@@ -84,11 +84,14 @@ def _check(calls, refs, what):
      ([1] * 20, 40, 512, "bf16", 9)],
     [([5, 9, 33, 2], 72, 1024, "f32", None)] * 4,
     [([0, 0, 0], 64, 512, "bf16", None), ([7, 1], 30, 512, "bf16", None)],
+    [([63, 64, 65, 0, 129], 136, 1024, "bf16", 300), ([5, 9, 33, 2], 72, 1024, "f32", None),
+     ([200, 3], 64, 512, "f32", None)],
 ])
 def test_problems_in_one_launch(specs):
     """Ragged groups (empty experts, chunks of one and two token fragments,
-    ragged weight tiles), mixed K, N and output types, with and without a
-    routing index, up to the four-problem limit."""
+    experts of up to 200 rows, ragged weight tiles),
+    mixed K, N and output types, with and without a routing index, up to the
+    four-problem limit."""
     need_gpu()
     rng = np.random.default_rng(sum(len(s[0]) + s[1] + s[2] for s in specs))
     pairs = [_problem(rng, *s) for s in specs]
